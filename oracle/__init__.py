@@ -1,0 +1,215 @@
+"""fp64 CPU oracle of Orthros attention: TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+may import this package. The product path (the HIP library and its Python
+binding) never imports, links or calls it, and the two share no code.
+
+The arithmetic lives in ``orthros_oracle.c`` (plain C, fp64, two-pass
+softmax per row); this module only marshals numpy arrays. Each function
+names the passage of the pages it follows:
+
+* ``swa``         base-stream sliding-window attention, o_t
+                  (Orthros: Phase-Aware Heterogeneous Attention for
+                  Efficient Transformers, paper text §3.1, the o_t equation)
+* ``xattn``       output-stream full cross-attention, o'_t
+                  (same page, §3.1, the o'_t equation; rows t = T_in + r)
+* ``row_weights`` normalised weights of one row (support / sum checks)
+* ``Cache``       incremental prefill-then-decode, the decode pair step
+                  (same page, §3.2 Decoding)
+
+Parity pins (tests/test_oracle_pins.py) tie every function to something
+other than itself: torch's scaled_dot_product_attention for the cases that
+reduce to standard causal or masked attention, closed forms, exact index
+supports, and incremental == batched.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liborthros_oracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b  # noqa: WPS433 (build on first use)
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    c_int, c_i64, c_void = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_swa.argtypes = [c_int, c_int, c_int, c_int, c_int, c_i64, _i32p,
+                               _dp, _dp, _dp, _dp, _dp, _dp, _dp, c_i64, _i64p]
+    lib.oracle_swa.restype = c_int
+    lib.oracle_xattn.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int,
+                                 _i32p, _dp, _dp, _dp, _dp, _dp, _dp, _dp,
+                                 c_i64, _i64p]
+    lib.oracle_xattn.restype = c_int
+    lib.oracle_row_weights.argtypes = [c_int, c_int, c_int, c_i64, c_i64,
+                                       c_int, _dp, _dp, _dp, _dp, _dp, _dp]
+    lib.oracle_row_weights.restype = c_int
+    lib.oracle_cache_new.argtypes = [c_int, c_int, c_int, c_i64]
+    lib.oracle_cache_new.restype = c_void
+    lib.oracle_cache_free.argtypes = [c_void]
+    lib.oracle_cache_free.restype = None
+    lib.oracle_cache_len.argtypes = [c_void, c_int]
+    lib.oracle_cache_len.restype = c_i64
+    lib.oracle_cache_append.argtypes = [c_void, c_int, _dp, _dp]
+    lib.oracle_cache_append.restype = c_int
+    lib.oracle_cache_decode_pair.argtypes = [c_void, c_int, c_i64, _i32p,
+                                             _dp, _dp, _dp, _dp, _dp, _dp,
+                                             _dp, _dp, _dp, _dp]
+    lib.oracle_cache_decode_pair.restype = c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a, typ=_dp):
+    return None if a is None else a.ctypes.data_as(typ)
+
+
+def _map(head_map):
+    if head_map is None:
+        return None
+    return np.ascontiguousarray(head_map, dtype=np.int32)
+
+
+def _rows(rows):
+    if rows is None:
+        return None, 0
+    r = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 2)
+    return r, r.shape[0]
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_num_threads())
+
+
+def swa(q_pre, alpha, beta, k, v, W, head_map=None, rows=None):
+    """Base-stream SWA, every position t: keys [max(0, t-W+1), t].
+
+    q_pre [B,T,Hq,D]; alpha, beta [Hq*D] (or [Hq,D]); k, v [B,T,Hkv,D].
+    rows: optional (n,2) int array of (b, t) to evaluate; outputs are then
+    [n, Hq, D] / [n, Hq] instead of [B,T,Hq,D] / [B,T,Hq].
+    Returns (o, lse) as float64.
+    """
+    lib = _load()
+    q_pre, k, v = _f64(q_pre), _f64(k), _f64(v)
+    alpha, beta = _f64(alpha).reshape(-1), _f64(beta).reshape(-1)
+    B, T, Hq, D = q_pre.shape
+    Hkv = k.shape[2]
+    assert k.shape == (B, T, Hkv, D) and v.shape == k.shape
+    assert alpha.size == Hq * D and beta.size == Hq * D
+    hm = _map(head_map)
+    r, n = _rows(rows)
+    lead = (n,) if r is not None else (B, T)
+    o = np.empty(lead + (Hq, D))
+    lse = np.empty(lead + (Hq,))
+    rc = lib.oracle_swa(B, T, Hq, Hkv, D, int(W), _ptr(hm, _i32p),
+                        _ptr(q_pre), _ptr(alpha), _ptr(beta), _ptr(k),
+                        _ptr(v), _ptr(o), _ptr(lse), n, _ptr(r, _i64p))
+    if rc:
+        raise ValueError("oracle_swa: invalid arguments")
+    return o, lse
+
+
+def xattn(qx_pre, alpha_x, beta_x, k, v, T_in, head_map=None, rows=None):
+    """Output-stream cross-attention: row r sits at t = T_in + r and attends
+    keys [0, t]. qx_pre [B,T_out,Hq,D]; k, v [B,T,Hkv,D] with T >= T_in+T_out
+    (only the first T_in + T_out keys are visible).
+    rows: optional (n,2) array of (b, r). Returns (o_x, lse)."""
+    lib = _load()
+    qx_pre = _f64(qx_pre)
+    alpha_x, beta_x = _f64(alpha_x).reshape(-1), _f64(beta_x).reshape(-1)
+    B, T_out, Hq, D = qx_pre.shape
+    T = T_in + T_out
+    k = _f64(k[:, :T])
+    v = _f64(v[:, :T])
+    Hkv = k.shape[2]
+    assert k.shape == (B, T, Hkv, D)
+    hm = _map(head_map)
+    r, n = _rows(rows)
+    lead = (n,) if r is not None else (B, T_out)
+    o = np.empty(lead + (Hq, D))
+    lse = np.empty(lead + (Hq,))
+    rc = lib.oracle_xattn(B, int(T_in), T_out, Hq, Hkv, D, _ptr(hm, _i32p),
+                          _ptr(qx_pre), _ptr(alpha_x), _ptr(beta_x), _ptr(k),
+                          _ptr(v), _ptr(o), _ptr(lse), n, _ptr(r, _i64p))
+    if rc:
+        raise ValueError("oracle_xattn: invalid arguments")
+    return o, lse
+
+
+def row_weights(q_pre_row, alpha_h, beta_h, k_b, v_b, t, W, g):
+    """Normalised weights over all T keys for one query row at position t
+    (W <= 0: unbounded window). k_b, v_b [T,Hkv,D] of one batch entry."""
+    lib = _load()
+    k_b, v_b = _f64(k_b), _f64(v_b)
+    T, Hkv, D = k_b.shape
+    w = np.empty(T)
+    rc = lib.oracle_row_weights(T, Hkv, D, int(t), int(W), int(g),
+                                _ptr(_f64(q_pre_row)), _ptr(_f64(alpha_h)),
+                                _ptr(_f64(beta_h)), _ptr(k_b), _ptr(v_b),
+                                _ptr(w))
+    if rc:
+        raise ValueError("oracle_row_weights: invalid arguments")
+    return w
+
+
+class Cache:
+    """Growing per-layer K/V cache of the base stream (incremental mode)."""
+
+    def __init__(self, B, Hkv, D, cap):
+        self._lib = _load()
+        self.B, self.Hkv, self.D, self.cap = B, Hkv, D, cap
+        self._h = self._lib.oracle_cache_new(B, Hkv, D, int(cap))
+        if not self._h:
+            raise MemoryError("oracle cache allocation failed")
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._lib.oracle_cache_free(h)
+
+    def length(self, b):
+        return int(self._lib.oracle_cache_len(self._h, b))
+
+    def append(self, k_new, v_new):
+        """k_new, v_new [B, n, Hkv, D]."""
+        k_new, v_new = _f64(k_new), _f64(v_new)
+        n = k_new.shape[1]
+        assert k_new.shape == (self.B, n, self.Hkv, self.D)
+        if self._lib.oracle_cache_append(self._h, n, _ptr(k_new), _ptr(v_new)):
+            raise ValueError("oracle cache append: capacity exceeded")
+
+    def decode_pair(self, q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
+                    k_new, v_new, W, head_map=None):
+        """Append one base token, then base SWA + output full attention.
+        q_pre, qx_pre [B,Hq,D]; k_new, v_new [B,Hkv,D]. Returns (o, o_x)."""
+        q_pre, qx_pre = _f64(q_pre), _f64(qx_pre)
+        B, Hq, D = q_pre.shape
+        o = np.empty((B, Hq, D))
+        o_x = np.empty((B, Hq, D))
+        hm = _map(head_map)
+        rc = self._lib.oracle_cache_decode_pair(
+            self._h, Hq, int(W), _ptr(hm, _i32p), _ptr(q_pre), _ptr(qx_pre),
+            _ptr(_f64(alpha).reshape(-1)), _ptr(_f64(beta).reshape(-1)),
+            _ptr(_f64(alpha_x).reshape(-1)), _ptr(_f64(beta_x).reshape(-1)),
+            _ptr(_f64(k_new)), _ptr(_f64(v_new)), _ptr(o), _ptr(o_x))
+        if rc:
+            raise ValueError("oracle decode_pair: invalid arguments")
+        return o, o_x
