@@ -1,0 +1,241 @@
+/*
+ * orthros.h - C ABI of the Orthros attention hot path for AMD MI355X (gfx950).
+ *
+ * Orthros attention keeps two token streams in one layer (pages: "Orthros:
+ * Phase-Aware Heterogeneous Attention for Efficient Transformers", paper
+ * text §3.1; the paper-notes page of the same title, key designs 1-3):
+ *
+ *   base stream    q_t  = alpha  (.) (x_t W_Q) + beta    for every position
+ *                  o_t  = softmax over keys [t-W+1, t] (window W) of
+ *                         q_t . k_j / sqrt(D), applied to V
+ *   output stream  q'_t = alpha' (.) (x'_t W_Q) + beta'  for the last T_out
+ *                         positions only
+ *                  o'_t = softmax over keys [0, t] of q'_t . k_j / sqrt(D),
+ *                         applied to V
+ *
+ * K/V come from the base stream only and form the full per-layer cache that
+ * both streams read; the output stream never writes K/V (reproduction note
+ * "Orthros：阶段异构注意力", background section). The library takes the
+ * projected, pre-affine queries and the projected K/V; the projections and
+ * W_O are the caller's.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  * Indices are 0-based: position t of the pages' 1-based formulas is t-1
+ *    here, so the base range is [max(0, t-W+1), t] (exactly min(t+1, W) keys)
+ *    and the output range is [0, t].
+ *  * Device pointers (marked [dev]) point to device memory owned by the
+ *    caller; the library never allocates or frees device memory and keeps no
+ *    pointer after a call returns. Tensors are dense, row-major, no strides.
+ *    Host pointers are marked [host] and are read before the call returns.
+ *  * Element type `dtype`: ORTHROS_F32 or ORTHROS_BF16 for Q, K, V and the
+ *    outputs. alpha/beta vectors are always fp32 with Hq*D entries (one per
+ *    channel of the query projection, head-major). Accumulation is fp32.
+ *  * D is the per-head dimension and the one in sqrt(D).
+ *  * head_map [host] int32[Hq]: KV head read by each query head, values in
+ *    [0, Hkv); NULL means the contiguous grouping h / (Hq/Hkv), which then
+ *    requires Hq % Hkv == 0.
+ *  * K/V cache layout: [B, Hkv, cap, D] (rows 0..cap-1 per batch entry and
+ *    KV head); projection layout of new K/V: [B, n, Hkv, D].
+ *  * All arguments are validated on the host before any HIP call. On error
+ *    the call returns a negative ORTHROS_E* code, launches nothing and
+ *    records a message readable with orthros_last_error() (thread-local).
+ *  * Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream). Nothing is synchronised; results are ready when the
+ *    stream is. Calls that share buffers must be ordered by the caller.
+ *  * Zero-sized work (B == 0, T == 0, n_new == 0) returns ORTHROS_OK and
+ *    launches nothing.
+ *  * Device-side capacity faults (a cache length that would exceed cap)
+ *    never write out of bounds: the affected batch entry is skipped and a
+ *    sticky device flag is raised, reported by orthros_check_device_errors.
+ */
+#ifndef ORTHROS_H
+#define ORTHROS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORTHROS_ABI_VERSION 1
+
+/* dtype codes */
+#define ORTHROS_F32 0
+#define ORTHROS_BF16 1
+
+/* status codes */
+#define ORTHROS_OK 0
+#define ORTHROS_EINVAL (-1)       /* bad pointer, size, range or head map */
+#define ORTHROS_EUNSUPPORTED (-2) /* dtype or head dimension not supported */
+#define ORTHROS_ECAPACITY (-3)    /* cache capacity would be exceeded */
+#define ORTHROS_EWORKSPACE (-4)   /* workspace missing or too small */
+#define ORTHROS_EHIP (-5)         /* a HIP runtime call failed */
+
+/* workspace query operation codes */
+#define ORTHROS_OP_GLOBAL_XATTN 1
+#define ORTHROS_OP_DECODE_PAIR 2
+
+/* Largest supported head dimension, query-head count and cache capacity. */
+#define ORTHROS_MAX_D 256
+#define ORTHROS_MAX_HEADS 128
+
+/*
+ * orthros_kv_append - materialise base-stream K/V in the per-layer cache.
+ *
+ * Pages: paper text §3.1 (k_i = x_i W_K and v_i = x_i W_V for every base
+ * position, forming the layer-wise cache); reproduction note, background
+ * section (only the base stream writes K/V; the full cache is kept and grows
+ * by one row per decode step).
+ *
+ * For every batch entry b, rows cache_len[b] .. cache_len[b]+n_new-1 of
+ * k_cache/v_cache receive k_new[b, 0..n_new-1] / v_new[b, ...]; then
+ * cache_len[b] += n_new. A prefill calls it once with n_new = T on an empty
+ * cache (cache_len = 0).
+ *
+ *   k_cache, v_cache [dev] [B, Hkv, cap, D] dtype, written
+ *   cache_len        [dev] int32[B], read then advanced
+ *   k_new, v_new     [dev] [B, n_new, Hkv, D] dtype, read
+ * Errors: EINVAL (null pointer, negative size), EUNSUPPORTED (dtype, D),
+ * EHIP. A batch entry whose new length would exceed cap is skipped and the
+ * device flag is raised (ECAPACITY from orthros_check_device_errors).
+ */
+int orthros_kv_append(void *k_cache, void *v_cache, int32_t *cache_len,
+                      const void *k_new, const void *v_new, int B, int n_new,
+                      int Hkv, int D, int64_t cap, int dtype, void *stream);
+
+/*
+ * orthros_swa_prefill - base-stream sliding-window attention, every position.
+ *
+ * Pages: paper text §3.1, the o_t equation (window w) and the base-query
+ * scale-offset; paper-notes page, key designs 1 and 2 (same formulas; the
+ * base branch is a local-window attention); reproduction note, mapping
+ * section (a local T x window view, never a dense T x T mask).
+ *
+ * For b < B, t < T, query head h with KV head g = map(h):
+ *   q   = alpha[h*D..] (.) q_pre[b,t,h,:] + beta[h*D..]
+ *   o[b,t,h,:] = sum_{j=max(0,t-W+1)}^{t} softmax_j(q . k_j / sqrt(D)) v_j
+ * with k_j = k_cache[b,g,j,:], v_j = v_cache[b,g,j,:]; rows 0..T-1 of the
+ * cache must be valid (orthros_kv_append). W >= T gives full causal
+ * attention over the prefix (with identity alpha/beta: standard causal
+ * attention).
+ *
+ *   q_pre        [dev] [B, T, Hq, D] dtype (pre-affine projected queries)
+ *   alpha, beta  [dev] fp32 [Hq*D]
+ *   k_cache, v_cache [dev] [B, Hkv, cap, D] dtype, cap >= T
+ *   o            [dev] [B, T, Hq, D] dtype, written
+ *   W            window, >= 1
+ * Errors: EINVAL, EUNSUPPORTED, EHIP.
+ */
+int orthros_swa_prefill(const void *q_pre, const float *alpha,
+                        const float *beta, const void *k_cache,
+                        const void *v_cache, void *o, int B, int T, int Hq,
+                        int Hkv, int D, int64_t cap, int W,
+                        const int32_t *head_map, int dtype, void *stream);
+
+/*
+ * orthros_global_xattn - output-stream full cross-attention.
+ *
+ * Pages: paper text §3.1, the o'_t equation and the output-query
+ * scale-offset (computed only for the last T_out positions); §3.2 for the
+ * (T_in, T_out) settings: prefilling T_in = T-1, T_out = 1; SFT
+ * T_out = response length; pre-training T_in = 0, T_out = T; paper-notes
+ * page, key design 3 (the cross branch is an attention with unbounded
+ * window over the shared cache).
+ *
+ * Output row r (0 <= r < T_out) sits at position t = T_in + r:
+ *   q'  = alpha_x (.) qx_pre[b,r,h,:] + beta_x
+ *   o_x[b,r,h,:] = sum_{j=0}^{t} softmax_j(q' . k_j / sqrt(D)) v_j
+ * Cache rows 0..T_in+T_out-1 must be valid.
+ *
+ *   qx_pre       [dev] [B, T_out, Hq, D] dtype
+ *   alpha_x, beta_x [dev] fp32 [Hq*D]
+ *   k_cache, v_cache [dev] [B, Hkv, cap, D], cap >= T_in + T_out
+ *   o_x          [dev] [B, T_out, Hq, D] dtype, written
+ *   ws, ws_bytes [dev] scratch of at least orthros_workspace_bytes(
+ *                ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D, T_out, T_in+T_out)
+ *                bytes (may be NULL when that size is 0); contents on entry
+ *                are ignored and left undefined.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
+ */
+int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
+                         const float *beta_x, const void *k_cache,
+                         const void *v_cache, void *o_x, int B, int T_in,
+                         int T_out, int Hq, int Hkv, int D, int64_t cap,
+                         const int32_t *head_map, int dtype, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/*
+ * orthros_decode_pair - one decoding step of the decoupled token pair.
+ *
+ * Pages: paper text §3.1 (each decoding step processes a decoupled pair: one
+ * token runs the window attention and updates the cache, the other runs full
+ * cross-attention to predict the next output) and §3.2 Decoding (T = 1,
+ * T_out = 1); paper-notes page, key design 4.
+ *
+ * For each batch entry b with old length n = cache_len[b]:
+ *   1. append: k_cache[b,g,n,:] = k_new[b,g,:], v_cache likewise;
+ *   2. base query   q  = alpha (.) q_pre[b,h,:] + beta, keys [max(0,n-W+1), n]
+ *      -> o[b,h,:]
+ *   3. output query q' = alpha_x (.) qx_pre[b,h,:] + beta_x, keys [0, n]
+ *      -> o_x[b,h,:]
+ *   4. cache_len[b] = n + 1 (after both attentions have read the cache).
+ * Reading: the base token's own K/V is appended before it attends, so its
+ * window contains itself, as in the prefill formula.
+ *
+ *   q_pre, qx_pre      [dev] [B, Hq, D] dtype
+ *   alpha, beta, alpha_x, beta_x [dev] fp32 [Hq*D]
+ *   k_new, v_new       [dev] [B, Hkv, D] dtype
+ *   k_cache, v_cache   [dev] [B, Hkv, cap, D], appended in place
+ *   cache_len          [dev] int32[B], read then advanced by one
+ *   o, o_x             [dev] [B, Hq, D] dtype, written
+ *   max_len_after      host upper bound of cache_len[b] + 1 over all b,
+ *                      1 <= max_len_after <= cap (sizes the launch). A batch
+ *                      entry exceeding it is skipped and the device flag is
+ *                      raised.
+ *   W                  base window, >= 1
+ *   ws, ws_bytes       scratch of orthros_workspace_bytes(
+ *                      ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after)
+ * Errors: EINVAL, EUNSUPPORTED, ECAPACITY (max_len_after > cap), EWORKSPACE,
+ * EHIP.
+ */
+int orthros_decode_pair(const void *q_pre, const void *qx_pre,
+                        const float *alpha, const float *beta,
+                        const float *alpha_x, const float *beta_x,
+                        const void *k_new, const void *v_new, void *k_cache,
+                        void *v_cache, int32_t *cache_len, void *o, void *o_x,
+                        int B, int Hq, int Hkv, int D, int64_t cap,
+                        int64_t max_len_after, int W, const int32_t *head_map,
+                        int dtype, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Scratch bytes needed by orthros_global_xattn (op ORTHROS_OP_GLOBAL_XATTN,
+ * max_len = T_in + T_out) or orthros_decode_pair (op ORTHROS_OP_DECODE_PAIR,
+ * T_out = 1, max_len = max_len_after). Returns 0 for an unknown op or
+ * invalid sizes. Pure host function.
+ */
+size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
+                               int T_out, int64_t max_len);
+
+/* Static description of a status code. */
+const char *orthros_strerror(int code);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char *orthros_last_error(void);
+
+/*
+ * Synchronises `stream`, then reads and clears the sticky device flag raised
+ * by a capacity fault in orthros_kv_append / orthros_decode_pair on the
+ * current device. Returns ORTHROS_OK, ORTHROS_ECAPACITY or ORTHROS_EHIP.
+ */
+int orthros_check_device_errors(void *stream);
+
+/* ORTHROS_ABI_VERSION of the built library. */
+int orthros_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORTHROS_H */

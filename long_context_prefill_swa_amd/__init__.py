@@ -1,0 +1,232 @@
+"""Python binding of liborthros.so, the gfx950 Orthros attention hot path.
+
+Argument marshalling only: every function below checks that the tensors are
+dense and on the GPU, derives the sizes from their shapes, and calls the C
+entry point of the same name with raw device pointers and the current HIP
+stream. All arithmetic happens in the library's HIP kernels. There is no CPU
+fallback: if the library is missing or fails to load, the functions raise.
+
+Layouts (see include/orthros.h for the full contract):
+  q_pre / o            [B, T, Hq, D]     qx_pre / o_x   [B, T_out, Hq, D]
+  k_cache / v_cache    [B, Hkv, cap, D]  k_new / v_new  [B, n, Hkv, D]
+  alpha, beta, ...     fp32 [Hq*D]       cache_len      int32 [B] (device)
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "ORTHROS_F32", "ORTHROS_BF16", "ORTHROS_OP_GLOBAL_XATTN",
+    "ORTHROS_OP_DECODE_PAIR", "OrthrosError", "lib", "library_path",
+    "orthros_kv_append", "orthros_swa_prefill", "orthros_global_xattn",
+    "orthros_decode_pair", "orthros_workspace_bytes",
+    "orthros_check_device_errors", "orthros_abi_version",
+    "orthros_strerror", "orthros_last_error", "workspace",
+]
+
+ORTHROS_F32 = 0
+ORTHROS_BF16 = 1
+ORTHROS_OP_GLOBAL_XATTN = 1
+ORTHROS_OP_DECODE_PAIR = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "liborthros.so")
+_lib = None
+
+
+class OrthrosError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"orthros error {code}: {message}")
+        self.code = code
+
+
+def lib():
+    """The loaded liborthros.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise OrthrosError(-5, f"{library_path} is missing: build it with "
+                               "`python -m long_context_prefill_swa_amd.build`")
+    L = ctypes.CDLL(library_path)
+    vp, i32, i64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                        ctypes.c_size_t)
+    L.orthros_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                    i64, i32, vp]
+    L.orthros_swa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                      i32, i32, i64, i32, vp, i32, vp]
+    L.orthros_global_xattn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                       i32, i32, i32, i64, vp, i32, vp, sz, vp]
+    L.orthros_decode_pair.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, i32, i32, i32, i32, i64,
+                                      i64, i32, vp, i32, vp, sz, vp]
+    L.orthros_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i64]
+    L.orthros_workspace_bytes.restype = sz
+    L.orthros_strerror.argtypes = [i32]
+    L.orthros_strerror.restype = ctypes.c_char_p
+    L.orthros_last_error.argtypes = []
+    L.orthros_last_error.restype = ctypes.c_char_p
+    L.orthros_check_device_errors.argtypes = [vp]
+    L.orthros_abi_version.argtypes = []
+    for name in ("orthros_kv_append", "orthros_swa_prefill",
+                 "orthros_global_xattn", "orthros_decode_pair",
+                 "orthros_check_device_errors", "orthros_abi_version"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != 0:
+        msg = lib().orthros_last_error().decode(errors="replace")
+        raise OrthrosError(rc, msg or orthros_strerror(rc))
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ORTHROS_BF16
+    if t.dtype == torch.float32:
+        return ORTHROS_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, like):
+    if stream is None:
+        stream = torch.cuda.current_stream(like.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _map(head_map):
+    if head_map is None:
+        return None, None
+    arr = (ctypes.c_int32 * len(head_map))(*[int(x) for x in head_map])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def orthros_strerror(code):
+    return lib().orthros_strerror(int(code)).decode()
+
+
+def orthros_last_error():
+    return lib().orthros_last_error().decode(errors="replace")
+
+
+def orthros_abi_version():
+    return int(lib().orthros_abi_version())
+
+
+def orthros_workspace_bytes(op, B, Hq, Hkv, D, T_out, max_len):
+    return int(lib().orthros_workspace_bytes(op, B, Hq, Hkv, D, T_out,
+                                             int(max_len)))
+
+
+def workspace(nbytes, device):
+    """Caller-owned scratch buffer (16-byte aligned) for the split-KV calls."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def orthros_kv_append(k_cache, v_cache, cache_len, k_new, v_new, stream=None):
+    B, Hkv, cap, D = k_cache.shape
+    n_new = k_new.shape[1]
+    if tuple(k_new.shape) != (B, n_new, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, n, Hkv, D]")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    dt = k_cache.dtype
+    _check(lib().orthros_kv_append(
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(cache_len, "cache_len", torch.int32), _dev(k_new, "k_new", dt),
+        _dev(v_new, "v_new", dt), B, n_new, Hkv, D, cap, _dtype_code(k_cache),
+        _stream(stream, k_cache)))
+
+
+def orthros_swa_prefill(q_pre, alpha, beta, k_cache, v_cache, o, W,
+                        head_map=None, stream=None):
+    B, T, Hq, D = q_pre.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, Hkv, cap, D]")
+    if o.shape != q_pre.shape:
+        raise ValueError("o must have q_pre's shape")
+    dt = q_pre.dtype
+    hm, _keep = _map(head_map)
+    _check(lib().orthros_swa_prefill(
+        _dev(q_pre, "q_pre", dt), _dev(alpha, "alpha", torch.float32),
+        _dev(beta, "beta", torch.float32), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), _dev(o, "o", dt), B, T, Hq, Hkv, D, cap,
+        int(W), hm, _dtype_code(q_pre), _stream(stream, q_pre)))
+
+
+def orthros_global_xattn(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, T_in,
+                         head_map=None, ws=None, stream=None):
+    B, T_out, Hq, D = qx_pre.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, Hkv, cap, D]")
+    if o_x.shape != qx_pre.shape:
+        raise ValueError("o_x must have qx_pre's shape")
+    dt = qx_pre.dtype
+    if ws is None:
+        need = orthros_workspace_bytes(ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D,
+                                       T_out, int(T_in) + T_out)
+        ws = workspace(need, qx_pre.device) if need else None
+    hm, _keep = _map(head_map)
+    _check(lib().orthros_global_xattn(
+        _dev(qx_pre, "qx_pre", dt), _dev(alpha_x, "alpha_x", torch.float32),
+        _dev(beta_x, "beta_x", torch.float32), _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), _dev(o_x, "o_x", dt), B, int(T_in),
+        T_out, Hq, Hkv, D, cap, hm, _dtype_code(qx_pre), _dev(ws, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream, qx_pre)))
+
+
+def orthros_decode_pair(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
+                        v_new, k_cache, v_cache, cache_len, o, o_x,
+                        max_len_after, W, head_map=None, ws=None, stream=None):
+    B, Hq, D = q_pre.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, Hkv, cap, D]")
+    if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, Hkv, D]")
+    if qx_pre.shape != q_pre.shape or o.shape != q_pre.shape or o_x.shape != q_pre.shape:
+        raise ValueError("q_pre, qx_pre, o, o_x must all be [B, Hq, D]")
+    dt = q_pre.dtype
+    if ws is None:
+        need = orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D,
+                                       1, int(max_len_after))
+        ws = workspace(need, q_pre.device) if need else None
+    hm, _keep = _map(head_map)
+    f32 = torch.float32
+    _check(lib().orthros_decode_pair(
+        _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt),
+        _dev(alpha, "alpha", f32), _dev(beta, "beta", f32),
+        _dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32),
+        _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        _dev(cache_len, "cache_len", torch.int32), _dev(o, "o", dt),
+        _dev(o_x, "o_x", dt), B, Hq, Hkv, D, cap, int(max_len_after), int(W),
+        hm, _dtype_code(q_pre), _dev(ws, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream, q_pre)))
+
+
+def orthros_check_device_errors(stream=None, device=None):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    _check(lib().orthros_check_device_errors(ctypes.c_void_p(stream.cuda_stream)))

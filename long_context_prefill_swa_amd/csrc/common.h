@@ -1,0 +1,107 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace orthros {
+
+constexpr int kMaxHeads = 128;
+constexpr int kMaxGroups = 128;
+constexpr int kMaxGroupSize = 8;  // query heads packed with one KV head
+
+// A query-head grouping passed by value to the kernels. Group i reads KV
+// head kv[i] and serves up to `gsize` query heads q[i][0..gsize) (-1 marks
+// an empty slot). Built on the host from the caller's head map.
+struct HeadGroups {
+  int n_groups;
+  int gsize;  // 1, 2, 4 or 8
+  uint8_t kv[kMaxGroups];
+  int8_t q[kMaxGroups][kMaxGroupSize];
+};
+
+// Plain per-query-head map (generic kernels).
+struct HeadMap {
+  uint8_t kv_of_q[kMaxHeads];
+};
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// log2(e): scores are scaled into the base-2 domain once, at the query.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// ---- launchers (defined in the .hip files) --------------------------------
+
+// Sticky device error flag (capacity faults); address on the current device.
+hipError_t device_flag_ptr(int **out);
+
+// Copies new rows into the cache at cache_len[b]; a batch entry whose new
+// length would exceed `cap` is skipped and raises *flag. With bump != 0 the
+// lengths are then advanced (a second kernel).
+hipError_t launch_kv_append(void *k_cache, void *v_cache, int32_t *cache_len,
+                            const void *k_new, const void *v_new, int B,
+                            int n_new, int Hkv, int row_bytes, int64_t cap,
+                            int64_t cap_stride, int *flag, int bump,
+                            hipStream_t stream);
+
+// Generic row-per-wave attention for any D <= 256, fp32 or bf16.
+// Row r of batch b sits at position t = (cache_len ? cache_len[b] : q_offset)
+// + r and attends keys [max(0, t-W+1), t] (W <= 0: [0, t]); rows with
+// t >= t_limit (a rejected decode length) get zeros.
+hipError_t launch_rowwise(const void *q, const float *alpha, const float *beta,
+                          const void *k_cache, const void *v_cache, void *o,
+                          int B, int nrows, int Hq, int Hkv, int D,
+                          int64_t cap, int64_t t_limit, int64_t q_offset,
+                          int W, const int32_t *cache_len, const HeadMap &map,
+                          int is_bf16, hipStream_t stream);
+
+// Increments cache_len[b] by n where the result stays within [0, cap].
+hipError_t launch_len_bump(int32_t *cache_len, int B, int n, int64_t cap,
+                           hipStream_t stream);
+
+// Banded flash attention, bf16, D = 128, MFMA. Rows r in [0, nrows) sit at
+// positions q_offset + r; keys [max(0, t-W+1), t] (W <= 0: unbounded).
+hipError_t launch_band_mfma(const void *q, const float *alpha,
+                            const float *beta, const void *k_cache,
+                            const void *v_cache, void *o, int B, int nrows,
+                            int Hq, int64_t cap, int64_t q_offset, int W,
+                            const HeadGroups &groups, int n_kv,
+                            hipStream_t stream);
+
+// Split-KV flash decode, bf16, D = 128, MFMA. See splitkv_mfma.hip.
+struct SplitKVArgs {
+  const void *q[2];          // [B, n_pos, Hq, D] per stream
+  const float *alpha[2];
+  const float *beta[2];
+  void *o[2];                // [B, n_pos, Hq, D] per stream
+  int W[2];                  // window per stream (<= 0: unbounded)
+  int n_streams;             // 1 (global) or 2 (decode pair)
+  int n_pos;                 // query positions per stream
+  int B, Hq, n_kv_heads;
+  int64_t cap;
+  int64_t pos0;              // position of q row 0 (host known) ...
+  const int32_t *cache_len;  // ... or, if non-null, cache_len[b] (decode)
+  void *k_cache, *v_cache;
+  const void *k_new, *v_new; // decode: appended row [B, Hkv, D]
+  int64_t max_len;           // upper bound of keys per batch entry
+  int chunk;                 // keys per split (multiple of 128)
+  int n_chunks;
+  float *ws;                 // partials: (max, sum) pairs, then outputs
+  int64_t ws_acc_offset;     // float offset of the unnormalised outputs
+  int32_t *ws_len;           // decode: per-batch old length or -1
+  int *flag;
+};
+int splitkv_rows(int n_streams, int n_pos, int gsize);
+size_t splitkv_ws_bytes(int B, int n_groups, int rows, int n_chunks, int D);
+int splitkv_pick_chunk(int B, int n_groups, int64_t max_len);
+hipError_t launch_splitkv(const SplitKVArgs &a, const HeadGroups &groups,
+                          hipStream_t stream);
+
+}  // namespace orthros

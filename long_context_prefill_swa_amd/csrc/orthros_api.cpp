@@ -1,0 +1,442 @@
+// C ABI of the Orthros attention hot path: host-side validation, head
+// grouping, workspace sizing and kernel selection. Every argument is checked
+// before the first HIP call; a failing call launches nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/orthros.h"
+#include "common.h"
+
+using namespace orthros;
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(const char *what, hipError_t e) {
+  return fail(ORTHROS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void clear_error() { g_msg[0] = '\0'; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == ORTHROS_F32 ? 4 : 2; }
+
+int check_dtype_d(int dtype, int D) {
+  if (dtype != ORTHROS_F32 && dtype != ORTHROS_BF16)
+    return fail(ORTHROS_EUNSUPPORTED, "dtype %d is not ORTHROS_F32 or ORTHROS_BF16", dtype);
+  if (D < 1 || D > ORTHROS_MAX_D)
+    return fail(ORTHROS_EUNSUPPORTED, "head dimension D=%d outside [1, %d]", D,
+                ORTHROS_MAX_D);
+  if (dtype == ORTHROS_BF16 && (D % 2) != 0)
+    return fail(ORTHROS_EUNSUPPORTED, "bf16 needs an even head dimension (D=%d)", D);
+  return ORTHROS_OK;
+}
+
+int check_heads(int Hq, int Hkv) {
+  if (Hq < 1 || Hkv < 1)
+    return fail(ORTHROS_EINVAL, "head counts must be >= 1 (Hq=%d, Hkv=%d)", Hq, Hkv);
+  if (Hq > ORTHROS_MAX_HEADS || Hkv > ORTHROS_MAX_HEADS)
+    return fail(ORTHROS_EINVAL, "head counts above %d (Hq=%d, Hkv=%d)",
+                ORTHROS_MAX_HEADS, Hq, Hkv);
+  return ORTHROS_OK;
+}
+
+// Resolves the query-head -> KV-head map into both kernel forms.
+int build_maps(const int32_t *head_map, int Hq, int Hkv, HeadMap *map,
+               HeadGroups *groups) {
+  int kv_of[kMaxHeads];
+  if (!head_map) {
+    if (Hq % Hkv != 0)
+      return fail(ORTHROS_EINVAL,
+                  "Hq=%d is not a multiple of Hkv=%d and no head map was given",
+                  Hq, Hkv);
+    for (int h = 0; h < Hq; ++h) kv_of[h] = h / (Hq / Hkv);
+  } else {
+    for (int h = 0; h < Hq; ++h) {
+      if (head_map[h] < 0 || head_map[h] >= Hkv)
+        return fail(ORTHROS_EINVAL, "head_map[%d]=%d outside [0, %d)", h,
+                    head_map[h], Hkv);
+      kv_of[h] = head_map[h];
+    }
+  }
+  memset(map, 0, sizeof(*map));
+  for (int h = 0; h < Hq; ++h) map->kv_of_q[h] = (uint8_t)kv_of[h];
+
+  // Groups: the query heads of each KV head, in head order, packed `gsize`
+  // at a time (gsize = the largest head count of a KV head, rounded up to a
+  // power of two, at most 8).
+  int count[kMaxHeads] = {0};
+  int maxc = 0;
+  for (int h = 0; h < Hq; ++h) maxc = std::max(maxc, ++count[kv_of[h]]);
+  int gsize = 1;
+  while (gsize < maxc && gsize < kMaxGroupSize) gsize *= 2;
+  memset(groups, 0, sizeof(*groups));
+  groups->gsize = gsize;
+  int n = 0;
+  for (int g = 0; g < Hkv; ++g) {
+    int slot = gsize;  // forces a new group on the first head
+    for (int h = 0; h < Hq; ++h) {
+      if (kv_of[h] != g) continue;
+      if (slot == gsize) {
+        if (n >= kMaxGroups) return fail(ORTHROS_EINVAL, "too many head groups");
+        groups->kv[n] = (uint8_t)g;
+        for (int s = 0; s < kMaxGroupSize; ++s) groups->q[n][s] = -1;
+        ++n;
+        slot = 0;
+      }
+      groups->q[n - 1][slot++] = (int8_t)h;
+    }
+  }
+  groups->n_groups = n;
+  return ORTHROS_OK;
+}
+
+// Overflow-safe product of non-negative sizes.
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool tensor_elems(int64_t *out, std::initializer_list<int64_t> dims) {
+  int64_t n = 1;
+  for (int64_t d : dims)
+    if (!mul_ok(n, d, &n)) return false;
+  *out = n;
+  return true;
+}
+
+bool mfma_eligible(int dtype, int D, std::initializer_list<const void *> ptrs) {
+  if (dtype != ORTHROS_BF16 || D != 128) return false;
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return false;
+  return true;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Split-KV plan shared by the workspace query and the launches.
+struct SplitPlan {
+  bool use = false;
+  int rows = 0, chunk = 0, n_chunks = 0;
+  size_t ws_bytes = 0;
+};
+
+SplitPlan plan_split(int B, int n_streams, int n_pos, const HeadGroups &g,
+                     int D, int64_t max_len) {
+  SplitPlan p;
+  p.rows = splitkv_rows(n_streams, n_pos, g.gsize);
+  if (D != 128 || p.rows > 16) return p;
+  p.use = true;
+  p.chunk = splitkv_pick_chunk(B, g.n_groups, max_len);
+  p.n_chunks = (int)((max_len + p.chunk - 1) / p.chunk);
+  p.ws_bytes = splitkv_ws_bytes(B, g.n_groups, p.rows, p.n_chunks, D);
+  return p;
+}
+
+void fill_ws(SplitKVArgs *a, void *ws, const SplitPlan &p, int B,
+             int n_groups) {
+  const size_t len_bytes = ((size_t)B * 4 + 255) / 256 * 256;
+  a->ws_len = (int32_t *)ws;
+  a->ws = (float *)((char *)ws + len_bytes);
+  const int64_t parts = (int64_t)B * n_groups * p.n_chunks * p.rows;
+  a->ws_acc_offset = (parts * 2 + 63) / 64 * 64;
+  a->chunk = p.chunk;
+  a->n_chunks = p.n_chunks;
+}
+
+}  // namespace
+
+extern "C" {
+
+int orthros_abi_version(void) { return ORTHROS_ABI_VERSION; }
+
+const char *orthros_strerror(int code) {
+  switch (code) {
+    case ORTHROS_OK: return "ok";
+    case ORTHROS_EINVAL: return "invalid argument";
+    case ORTHROS_EUNSUPPORTED: return "unsupported dtype or head dimension";
+    case ORTHROS_ECAPACITY: return "cache capacity exceeded";
+    case ORTHROS_EWORKSPACE: return "workspace missing or too small";
+    case ORTHROS_EHIP: return "HIP runtime error";
+    default: return "unknown status code";
+  }
+}
+
+const char *orthros_last_error(void) { return g_msg; }
+
+size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
+                               int T_out, int64_t max_len) {
+  if (B < 1 || T_out < 1 || max_len < 1 || D < 1 || D > ORTHROS_MAX_D)
+    return 0;
+  if (Hq < 1 || Hkv < 1 || Hq > ORTHROS_MAX_HEADS || Hkv > ORTHROS_MAX_HEADS ||
+      Hq % Hkv != 0)
+    return 0;
+  HeadMap map;
+  HeadGroups g;
+  const int saved = g_msg[0];
+  if (build_maps(nullptr, Hq, Hkv, &map, &g) != ORTHROS_OK) return 0;
+  if (!saved) clear_error();
+  SplitPlan p;
+  if (op == ORTHROS_OP_GLOBAL_XATTN)
+    p = plan_split(B, 1, T_out, g, D, max_len);
+  else if (op == ORTHROS_OP_DECODE_PAIR)
+    p = plan_split(B, 2, 1, g, D, max_len);
+  else
+    return 0;
+  return p.use ? p.ws_bytes : 0;
+}
+
+int orthros_kv_append(void *k_cache, void *v_cache, int32_t *cache_len,
+                      const void *k_new, const void *v_new, int B, int n_new,
+                      int Hkv, int D, int64_t cap, int dtype, void *stream) {
+  clear_error();
+  int rc = check_dtype_d(dtype, D);
+  if (rc) return rc;
+  if (B < 0 || n_new < 0) return fail(ORTHROS_EINVAL, "negative size (B=%d, n_new=%d)", B, n_new);
+  if (Hkv < 1 || Hkv > ORTHROS_MAX_HEADS) return fail(ORTHROS_EINVAL, "Hkv=%d outside [1, %d]", Hkv, ORTHROS_MAX_HEADS);
+  if (cap < 1 || cap > INT32_MAX) return fail(ORTHROS_EINVAL, "cap=%lld outside [1, 2^31-1]", (long long)cap);
+  if (n_new > cap) return fail(ORTHROS_ECAPACITY, "n_new=%d exceeds cap=%lld", n_new, (long long)cap);
+  if (B == 0 || n_new == 0) return ORTHROS_OK;
+  if (!k_cache || !v_cache || !cache_len || !k_new || !v_new)
+    return fail(ORTHROS_EINVAL, "null pointer argument");
+  int64_t n_elems;
+  if (!tensor_elems(&n_elems, {B, Hkv, cap, D, (int64_t)esize(dtype)}))
+    return fail(ORTHROS_EINVAL, "cache size overflows");
+  const int row_bytes = D * (int)esize(dtype);
+  int *flag = nullptr;
+  hipError_t e = device_flag_ptr(&flag);
+  if (e != hipSuccess) return hip_fail("device flag", e);
+  e = launch_kv_append(k_cache, v_cache, cache_len, k_new, v_new, B, n_new,
+                       Hkv, row_bytes, cap, cap, flag, 1, as_stream(stream));
+  if (e != hipSuccess) return hip_fail("kv_append launch", e);
+  return ORTHROS_OK;
+}
+
+int orthros_swa_prefill(const void *q_pre, const float *alpha,
+                        const float *beta, const void *k_cache,
+                        const void *v_cache, void *o, int B, int T, int Hq,
+                        int Hkv, int D, int64_t cap, int W,
+                        const int32_t *head_map, int dtype, void *stream) {
+  clear_error();
+  int rc = check_dtype_d(dtype, D);
+  if (rc) return rc;
+  if ((rc = check_heads(Hq, Hkv))) return rc;
+  if (B < 0 || T < 0) return fail(ORTHROS_EINVAL, "negative size (B=%d, T=%d)", B, T);
+  if (W < 1) return fail(ORTHROS_EINVAL, "window W=%d must be >= 1", W);
+  if (cap < T || cap > INT32_MAX)
+    return fail(ORTHROS_EINVAL, "cap=%lld must hold the T=%d rows", (long long)cap, T);
+  HeadMap map;
+  HeadGroups groups;
+  if ((rc = build_maps(head_map, Hq, Hkv, &map, &groups))) return rc;
+  if (B == 0 || T == 0) return ORTHROS_OK;
+  if (!q_pre || !alpha || !beta || !k_cache || !v_cache || !o)
+    return fail(ORTHROS_EINVAL, "null pointer argument");
+  int64_t n_elems;
+  if (!tensor_elems(&n_elems, {B, Hkv, cap, D, 2}) ||
+      !tensor_elems(&n_elems, {B, T, Hq, D, 2}))
+    return fail(ORTHROS_EINVAL, "tensor size overflows");
+  hipError_t e;
+  if (mfma_eligible(dtype, D, {q_pre, k_cache, v_cache, o})) {
+    e = launch_band_mfma(q_pre, alpha, beta, k_cache, v_cache, o, B, T, Hq,
+                         cap, 0, W, groups, Hkv, as_stream(stream));
+  } else {
+    e = launch_rowwise(q_pre, alpha, beta, k_cache, v_cache, o, B, T, Hq, Hkv,
+                       D, cap, cap, 0, W, nullptr, map,
+                       dtype == ORTHROS_BF16, as_stream(stream));
+  }
+  if (e != hipSuccess) return hip_fail("swa_prefill launch", e);
+  return ORTHROS_OK;
+}
+
+int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
+                         const float *beta_x, const void *k_cache,
+                         const void *v_cache, void *o_x, int B, int T_in,
+                         int T_out, int Hq, int Hkv, int D, int64_t cap,
+                         const int32_t *head_map, int dtype, void *ws,
+                         size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_dtype_d(dtype, D);
+  if (rc) return rc;
+  if ((rc = check_heads(Hq, Hkv))) return rc;
+  if (B < 0 || T_in < 0 || T_out < 0)
+    return fail(ORTHROS_EINVAL, "negative size (B=%d, T_in=%d, T_out=%d)", B, T_in, T_out);
+  const int64_t T = (int64_t)T_in + T_out;
+  if (cap < T || cap > INT32_MAX)
+    return fail(ORTHROS_EINVAL, "cap=%lld must hold T_in+T_out=%lld rows",
+                (long long)cap, (long long)T);
+  HeadMap map;
+  HeadGroups groups;
+  if ((rc = build_maps(head_map, Hq, Hkv, &map, &groups))) return rc;
+  if (B == 0 || T_out == 0) return ORTHROS_OK;
+  if (!qx_pre || !alpha_x || !beta_x || !k_cache || !v_cache || !o_x)
+    return fail(ORTHROS_EINVAL, "null pointer argument");
+  int64_t n_elems;
+  if (!tensor_elems(&n_elems, {B, Hkv, cap, D, 2}) ||
+      !tensor_elems(&n_elems, {B, T_out, Hq, D, 2}))
+    return fail(ORTHROS_EINVAL, "tensor size overflows");
+
+  hipError_t e;
+  const bool mfma = mfma_eligible(dtype, D, {qx_pre, k_cache, v_cache, o_x});
+  const SplitPlan plan = plan_split(B, 1, T_out, groups, D, T);
+  if (mfma && plan.use) {
+    if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))
+      return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
+                  plan.ws_bytes, ws ? ws_bytes : (size_t)0);
+    SplitKVArgs a = {};
+    a.q[0] = qx_pre;
+    a.alpha[0] = alpha_x;
+    a.beta[0] = beta_x;
+    a.o[0] = o_x;
+    a.W[0] = 0;
+    a.n_streams = 1;
+    a.n_pos = T_out;
+    a.B = B;
+    a.Hq = Hq;
+    a.n_kv_heads = Hkv;
+    a.cap = cap;
+    a.pos0 = T_in;
+    a.cache_len = nullptr;
+    a.k_cache = const_cast<void *>(k_cache);
+    a.v_cache = const_cast<void *>(v_cache);
+    a.max_len = T;
+    fill_ws(&a, ws, plan, B, groups.n_groups);
+    e = device_flag_ptr(&a.flag);
+    if (e != hipSuccess) return hip_fail("device flag", e);
+    e = launch_splitkv(a, groups, as_stream(stream));
+  } else if (mfma) {
+    e = launch_band_mfma(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, B,
+                         T_out, Hq, cap, T_in, 0, groups, Hkv,
+                         as_stream(stream));
+  } else {
+    e = launch_rowwise(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, B, T_out,
+                       Hq, Hkv, D, cap, cap, T_in, 0, nullptr, map,
+                       dtype == ORTHROS_BF16, as_stream(stream));
+  }
+  if (e != hipSuccess) return hip_fail("global_xattn launch", e);
+  return ORTHROS_OK;
+}
+
+int orthros_decode_pair(const void *q_pre, const void *qx_pre,
+                        const float *alpha, const float *beta,
+                        const float *alpha_x, const float *beta_x,
+                        const void *k_new, const void *v_new, void *k_cache,
+                        void *v_cache, int32_t *cache_len, void *o, void *o_x,
+                        int B, int Hq, int Hkv, int D, int64_t cap,
+                        int64_t max_len_after, int W, const int32_t *head_map,
+                        int dtype, void *ws, size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_dtype_d(dtype, D);
+  if (rc) return rc;
+  if ((rc = check_heads(Hq, Hkv))) return rc;
+  if (B < 0) return fail(ORTHROS_EINVAL, "negative batch B=%d", B);
+  if (W < 1) return fail(ORTHROS_EINVAL, "window W=%d must be >= 1", W);
+  if (cap < 1 || cap > INT32_MAX) return fail(ORTHROS_EINVAL, "cap=%lld outside [1, 2^31-1]", (long long)cap);
+  if (max_len_after < 1)
+    return fail(ORTHROS_EINVAL, "max_len_after=%lld must be >= 1", (long long)max_len_after);
+  if (max_len_after > cap)
+    return fail(ORTHROS_ECAPACITY, "max_len_after=%lld exceeds cap=%lld",
+                (long long)max_len_after, (long long)cap);
+  HeadMap map;
+  HeadGroups groups;
+  if ((rc = build_maps(head_map, Hq, Hkv, &map, &groups))) return rc;
+  if (B == 0) return ORTHROS_OK;
+  if (!q_pre || !qx_pre || !alpha || !beta || !alpha_x || !beta_x || !k_new ||
+      !v_new || !k_cache || !v_cache || !cache_len || !o || !o_x)
+    return fail(ORTHROS_EINVAL, "null pointer argument");
+  int64_t n_elems;
+  if (!tensor_elems(&n_elems, {B, Hkv, cap, D, 2}))
+    return fail(ORTHROS_EINVAL, "cache size overflows");
+
+  hipStream_t st = as_stream(stream);
+  const bool mfma = mfma_eligible(
+      dtype, D, {q_pre, qx_pre, k_new, v_new, k_cache, v_cache, o, o_x});
+  const SplitPlan plan = plan_split(B, 2, 1, groups, D, max_len_after);
+  if (mfma && plan.use && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)))
+    return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
+                plan.ws_bytes, ws ? ws_bytes : (size_t)0);
+  int *flag = nullptr;
+  hipError_t e = device_flag_ptr(&flag);
+  if (e != hipSuccess) return hip_fail("device flag", e);
+  if (mfma && plan.use) {
+    SplitKVArgs a = {};
+    a.q[0] = q_pre;
+    a.q[1] = qx_pre;
+    a.alpha[0] = alpha;
+    a.alpha[1] = alpha_x;
+    a.beta[0] = beta;
+    a.beta[1] = beta_x;
+    a.o[0] = o;
+    a.o[1] = o_x;
+    a.W[0] = W;
+    a.W[1] = 0;
+    a.n_streams = 2;
+    a.n_pos = 1;
+    a.B = B;
+    a.Hq = Hq;
+    a.n_kv_heads = Hkv;
+    a.cap = cap;
+    a.pos0 = 0;
+    a.cache_len = cache_len;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.max_len = max_len_after;
+    a.flag = flag;
+    fill_ws(&a, ws, plan, B, groups.n_groups);
+    e = launch_splitkv(a, groups, st);
+    if (e != hipSuccess) return hip_fail("decode_pair launch", e);
+    return ORTHROS_OK;
+  }
+  // Generic path: append (lengths unchanged), both attentions, then advance.
+  const int row_bytes = D * (int)esize(dtype);
+  e = launch_kv_append(k_cache, v_cache, cache_len, k_new, v_new, B, 1, Hkv,
+                       row_bytes, max_len_after, cap, flag, 0, st);
+  if (e == hipSuccess)
+    e = launch_rowwise(q_pre, alpha, beta, k_cache, v_cache, o, B, 1, Hq, Hkv,
+                       D, cap, max_len_after, 0, W, cache_len, map,
+                       dtype == ORTHROS_BF16, st);
+  if (e == hipSuccess)
+    e = launch_rowwise(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, B, 1,
+                       Hq, Hkv, D, cap, max_len_after, 0, 0, cache_len, map,
+                       dtype == ORTHROS_BF16, st);
+  if (e == hipSuccess) e = launch_len_bump(cache_len, B, 1, max_len_after, st);
+  if (e != hipSuccess) return hip_fail("decode_pair launch", e);
+  return ORTHROS_OK;
+}
+
+int orthros_check_device_errors(void *stream) {
+  clear_error();
+  hipError_t e = hipStreamSynchronize(as_stream(stream));
+  if (e != hipSuccess) return hip_fail("stream synchronize", e);
+  int *flag = nullptr;
+  e = device_flag_ptr(&flag);
+  if (e != hipSuccess) return hip_fail("device flag", e);
+  int host = 0;
+  e = hipMemcpy(&host, flag, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail("flag read", e);
+  if (!host) return ORTHROS_OK;
+  const int zero = 0;
+  e = hipMemcpy(flag, &zero, sizeof(int), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail("flag clear", e);
+  return fail(ORTHROS_ECAPACITY,
+              "a cache append or decode step exceeded the cache capacity; "
+              "the affected batch entries were skipped");
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host (before any HIP
+call) with the documented status codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from long_context_prefill_swa_amd import build as hipbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orthros.h")
+
+OK, EINVAL, EUNSUP, ECAP, EWS, EHIP = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+FAKE = 0x100000   # 16-byte aligned, never dereferenced by host validation
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(hipbuild.LIB):
+        hipbuild.build()
+    import long_context_prefill_swa_amd as m
+    return m.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*\*?\s*"
+                                 r"(orthros_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("orthros_kv_append", "orthros_swa_prefill",
+              "orthros_global_xattn", "orthros_decode_pair"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", hipbuild.LIB],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (orthros_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(L, n)
+
+
+def test_abi_version_and_strerror(L):
+    assert L.orthros_abi_version() == 1
+    for code in (OK, EINVAL, EUNSUP, ECAP, EWS, EHIP):
+        assert L.orthros_strerror(code)
+    assert b"unknown" in L.orthros_strerror(42)
+
+
+def last(L):
+    return L.orthros_last_error().decode()
+
+
+def swa(L, **kw):
+    a = dict(q=FAKE, al=FAKE, be=FAKE, k=FAKE, v=FAKE, o=FAKE, B=1, T=64,
+             Hq=4, Hkv=2, D=128, cap=64, W=16, hmap=None, dtype=BF16)
+    a.update(kw)
+    return L.orthros_swa_prefill(a["q"], a["al"], a["be"], a["k"], a["v"],
+                                 a["o"], a["B"], a["T"], a["Hq"], a["Hkv"],
+                                 a["D"], a["cap"], a["W"], a["hmap"],
+                                 a["dtype"], None)
+
+
+def hmap(vals):
+    arr = (ctypes.c_int32 * len(vals))(*vals)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=7), EUNSUP, "dtype"),
+    (dict(D=0), EUNSUP, "head dimension"),
+    (dict(D=257), EUNSUP, "head dimension"),
+    (dict(D=15), EUNSUP, "even"),
+    (dict(W=0), EINVAL, "window"),
+    (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
+    (dict(Hq=0), EINVAL, "head counts"),
+    (dict(Hq=129, Hkv=1), EINVAL, "head counts"),
+    (dict(cap=63), EINVAL, "cap"),
+    (dict(T=-1), EINVAL, "negative"),
+    (dict(q=None), EINVAL, "null"),
+    (dict(o=None), EINVAL, "null"),
+])
+def test_swa_prefill_rejects(L, kw, code, needle):
+    assert swa(L, **kw) == code
+    assert needle in last(L)
+
+
+def test_swa_prefill_head_map_checked(L):
+    p, keep = hmap([0, 1, 2, 1])       # KV head 2 does not exist (Hkv=2)
+    assert swa(L, hmap=p) == EINVAL and "head_map[2]" in last(L)
+    p, keep = hmap([0, 1, 1, 1])       # a valid uneven map passes validation
+    assert swa(L, hmap=p, B=0) == OK
+
+
+def test_zero_sized_calls_are_no_ops(L):
+    # return before any HIP call: valid even without a GPU
+    assert swa(L, B=0) == OK
+    assert swa(L, T=0) == OK
+    assert L.orthros_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, 2, 128,
+                               64, BF16, None) == OK
+    assert L.orthros_global_xattn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 10,
+                                  0, 4, 2, 128, 64, None, BF16, None, 0,
+                                  None) == OK
+
+
+def test_kv_append_rejects(L):
+    assert L.orthros_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 65, 2, 128,
+                               64, BF16, None) == ECAP
+    assert L.orthros_kv_append(FAKE, FAKE, None, FAKE, FAKE, 1, 4, 2, 128,
+                               64, BF16, None) == EINVAL
+    assert L.orthros_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 0, 128,
+                               64, BF16, None) == EINVAL
+    assert L.orthros_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, 2, 128,
+                               64, 3, None) == EUNSUP
+
+
+def test_global_xattn_rejects(L):
+    args = [FAKE] * 6 + [1, 100, 1, 4, 2, 128, 101, None, BF16]
+    # split-KV path needs a workspace
+    assert L.orthros_global_xattn(*args, None, 0, None) == EWS
+    assert "workspace" in last(L)
+    need = L.orthros_workspace_bytes(1, 1, 4, 2, 128, 1, 101)
+    assert need > 0
+    assert L.orthros_global_xattn(*args, FAKE, need - 1, None) == EWS
+    bad = [FAKE] * 6 + [1, 100, 1, 4, 2, 128, 100, None, BF16]   # cap < T
+    assert L.orthros_global_xattn(*bad, FAKE, need, None) == EINVAL
+
+
+def decode(L, **kw):
+    a = dict(B=2, Hq=4, Hkv=2, D=128, cap=100, max_len=50, W=16, ws=None,
+             ws_bytes=0, dtype=BF16, cl=FAKE)
+    a.update(kw)
+    ptrs = [FAKE] * 10
+    return L.orthros_decode_pair(*ptrs[:10], a["cl"], FAKE, FAKE, a["B"],
+                                 a["Hq"], a["Hkv"], a["D"], a["cap"],
+                                 a["max_len"], a["W"], None, a["dtype"],
+                                 a["ws"], a["ws_bytes"], None)
+
+
+def test_decode_pair_rejects(L):
+    assert decode(L, max_len=101) == ECAP
+    assert decode(L, max_len=0) == EINVAL
+    assert decode(L, W=0) == EINVAL
+    assert decode(L, cl=None) == EINVAL
+    assert decode(L) == EWS
+    assert decode(L, B=0) == OK
+
+
+def test_workspace_bytes(L):
+    ws = L.orthros_workspace_bytes
+    assert ws(9, 1, 4, 2, 128, 1, 100) == 0            # unknown op
+    assert ws(2, 0, 4, 2, 128, 1, 100) == 0            # empty batch
+    d1 = ws(2, 64, 32, 8, 128, 1, 33024)
+    d2 = ws(2, 64, 32, 8, 128, 1, 66048)
+    assert 0 < d1 < d2
+    # global pass with many output rows uses no workspace (banded kernel)
+    assert ws(1, 4, 32, 8, 128, 2048, 8192) == 0
+    # non-128 head dimensions run the generic kernel without workspace
+    assert ws(1, 1, 2, 2, 16, 1, 64) == 0

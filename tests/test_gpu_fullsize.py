@@ -1,0 +1,150 @@
+"""Full-size configurations on the GPU, in the launch configuration the
+benchmark times, checked against the fp64 oracle on sampled rows.
+
+A base-stream row t is checked by evaluating the oracle's softmax formula
+over exactly the key slice [max(0, t-W+1), t] (the output-stream routine over
+that slice with all of it visible), so the oracle never has to convert the
+whole query tensor. Sampled rows: the band edges t in {0, 1, W-2, W-1, W,
+T-2, T-1}, tile edges +-1 and seeded random rows, every batch entry, every
+head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import long_context_prefill_swa_amd as lo
+import oracle
+from gpu_util import compare, f64, say
+from workloads import (CONFIGS, affine_inputs, decode_all_steps, kv_inputs,
+                       prefill_inputs)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def sample_rows(T, W, n_random, seed):
+    base = {0, 1, W - 2, W - 1, W, T - 2, T - 1}
+    for e in (64, 128, 4096, T // 2):
+        for d in (-1, 0, 1):
+            base.add(e + d)
+    rng = np.random.default_rng(seed)
+    base.update(int(x) for x in rng.integers(0, T, n_random))
+    return sorted(t for t in base if 0 <= t < T)
+
+
+def check_rows(o, q, a, b, k_host, v_host, ts, W, what):
+    """o, q on GPU [B,T,Hq,D]; k_host, v_host float64 [B,T,Hkv,D]."""
+    got, ref = [], []
+    for t in ts:
+        lo_t = 0 if W is None else max(0, t - W + 1)
+        r, _ = oracle.xattn(f64(q[:, t:t + 1]), f64(a), f64(b),
+                            k_host[:, lo_t:t + 1], v_host[:, lo_t:t + 1],
+                            t - lo_t)
+        ref.append(r)
+        got.append(f64(o[:, t:t + 1]))
+    compare(np.concatenate(got, 1), np.concatenate(ref, 1), torch.bfloat16,
+            f"{what} ({len(ts)} rows x all heads)")
+
+
+def prefill(cfg, cfg_id, W=None):
+    W = cfg.W if W is None else W
+    x = prefill_inputs(cfg, cfg_id, DEV)
+    B, T, Hq, D = x.q_pre.shape
+    Hkv = cfg.Hkv
+    kc = torch.empty((B, Hkv, T, D), dtype=x.k.dtype, device=DEV)
+    vc = torch.empty_like(kc)
+    cl = torch.zeros(B, dtype=torch.int32, device=DEV)
+    lo.orthros_kv_append(kc, vc, cl, x.k, x.v)
+    o = torch.empty_like(x.q_pre)
+    lo.orthros_swa_prefill(x.q_pre, x.alpha, x.beta, kc, vc, o, W)
+    ox = torch.empty_like(x.qx_pre)
+    lo.orthros_global_xattn(x.qx_pre, x.alpha_x, x.beta_x, kc, vc, ox,
+                            cfg.T_in)
+    torch.cuda.synchronize()
+    assert cl.tolist() == [T] * B
+    return x, o, ox
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2, 4])
+def test_prefill_configuration_sampled(cfg_id):
+    cfg = CONFIGS[cfg_id]
+    say(f"[full size] {cfg.name}")
+    x, o, ox = prefill(cfg, cfg_id)
+    k_host, v_host = f64(x.k), f64(x.v)
+    ts = sample_rows(cfg.T, cfg.W, 24, cfg_id)
+    check_rows(o, x.q_pre, x.alpha, x.beta, k_host, v_host, ts, cfg.W,
+               "base stream")
+    # output stream: every row if few, else a sample
+    T_in = cfg.T_in
+    rs = (list(range(cfg.T_out)) if cfg.T_out <= 4 else
+          sample_rows(cfg.T_out, 64, 24, cfg_id + 100))
+    got, ref = [], []
+    for r in rs:
+        t = T_in + r
+        rr, _ = oracle.xattn(f64(x.qx_pre[:, r:r + 1]), f64(x.alpha_x),
+                             f64(x.beta_x), k_host[:, :t + 1], v_host[:, :t + 1], t)
+        ref.append(rr)
+        got.append(f64(ox[:, r:r + 1]))
+    compare(np.concatenate(got, 1), np.concatenate(ref, 1), torch.bfloat16,
+            f"output stream ({len(rs)} rows x all heads)")
+
+
+def test_long_prefill_full_causal_sampled():
+    """The same-T full causal run used for the speedup ratio (W = T)."""
+    cfg = CONFIGS[4]
+    say("[full size] prefill_128k full causal")
+    x, o, _ = prefill(cfg, 4, W=cfg.T)
+    k_host, v_host = f64(x.k), f64(x.v)
+    ts = [0, 1, 4095, 4096, 65535, cfg.T - 1]
+    check_rows(o, x.q_pre, x.alpha, x.beta, k_host, v_host, ts, None,
+               "causal")
+
+
+def test_decode_pair_configuration_sampled():
+    cfg = CONFIGS[3]
+    B, Hq, Hkv, D, L0, W = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.T, cfg.W
+    steps = cfg.decode_steps
+    say(f"[full size] {cfg.name}: {steps} steps")
+    k0, v0 = kv_inputs(cfg, 3, DEV)          # the 32768 cached tokens
+    st = decode_all_steps(cfg, 3, device=DEV)
+    cap = L0 + steps
+    kc = torch.empty((B, Hkv, cap, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    cl = torch.zeros(B, dtype=torch.int32, device=DEV)
+    lo.orthros_kv_append(kc, vc, cl, k0, v0)
+    del k0, v0
+    a, b, ax, bx = affine_inputs(cfg, 3, DEV)
+    keep = {0, 1, 127, 255}
+    outs = {}
+    ws = lo.workspace(lo.orthros_workspace_bytes(lo.ORTHROS_OP_DECODE_PAIR, B,
+                                                 Hq, Hkv, D, 1, cap), DEV)
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+    ox = torch.empty_like(o)
+    for s in range(steps):
+        lo.orthros_decode_pair(st.q_pre[s], st.qx_pre[s], a, b, ax, bx,
+                               st.k_new[s], st.v_new[s], kc, vc, cl, o, ox,
+                               max_len_after=L0 + s + 1, W=W, ws=ws)
+        if s in keep:
+            outs[s] = (o.clone(), ox.clone())
+    torch.cuda.synchronize()
+    assert cl.tolist() == [L0 + steps] * B, "cache lengths"
+    lo.orthros_check_device_errors()
+    bs = [0, 17, 42, 63]
+    for bi in bs:
+        kb = f64(kc[bi].permute(1, 0, 2))[None]     # [1, cap, Hkv, D]
+        vb = f64(vc[bi].permute(1, 0, 2))[None]
+        for s in sorted(keep):
+            n = L0 + s                               # index of the new key
+            lo_t = max(0, n - W + 1)
+            rb, _ = oracle.xattn(f64(st.q_pre[s][bi:bi + 1, None]), f64(a),
+                                 f64(b), kb[:, lo_t:n + 1], vb[:, lo_t:n + 1],
+                                 n - lo_t)
+            rx, _ = oracle.xattn(f64(st.qx_pre[s][bi:bi + 1, None]), f64(ax),
+                                 f64(bx), kb[:, :n + 1], vb[:, :n + 1], n)
+            compare(outs[s][0][bi:bi + 1, None], rb, torch.bfloat16,
+                    f"b={bi} step {s} base")
+            compare(outs[s][1][bi:bi + 1, None], rx, torch.bfloat16,
+                    f"b={bi} step {s} output")
+        # appended rows are the step tokens, bit for bit
+        assert torch.equal(kc[bi, :, L0:].permute(1, 0, 2).float(),
+                           st.k_new[:, bi].float())

@@ -101,19 +101,33 @@ class PrefillInputs:
     beta_x: torch.Tensor
 
 
+def affine_inputs(cfg: Config, cfg_id: int, device="cpu"):
+    """(alpha, beta, alpha_x, beta_x) of a configuration."""
+    s = lambda name: seed_of(cfg_id, name)  # noqa: E731
+    n = cfg.Hq * cfg.D
+    a, b = affine(n, s("alpha"), s("beta"), device, cfg.identity_affine)
+    ax, bx = affine(n, s("alpha_x"), s("beta_x"), device, cfg.identity_affine)
+    return a, b, ax, bx
+
+
+def kv_inputs(cfg: Config, cfg_id: int, device="cpu"):
+    """Base-stream K and V [B, T, Hkv, D] of a configuration."""
+    dt = cfg.torch_dtype
+    shape = (cfg.B, cfg.T, cfg.Hkv, cfg.D)
+    return (normal(shape, seed_of(cfg_id, "k"), dt, device),
+            normal(shape, seed_of(cfg_id, "v"), dt, device))
+
+
 def prefill_inputs(cfg: Config, cfg_id: int, device="cpu") -> PrefillInputs:
     dt = cfg.torch_dtype
-    B, T, Hq, Hkv, D = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.D
+    B, T, Hq, D = cfg.B, cfg.T, cfg.Hq, cfg.D
     s = lambda name: seed_of(cfg_id, name)  # noqa: E731
-    a, b = affine(Hq * D, s("alpha"), s("beta"), device, cfg.identity_affine)
-    ax, bx = affine(Hq * D, s("alpha_x"), s("beta_x"), device,
-                    cfg.identity_affine)
+    a, b, ax, bx = affine_inputs(cfg, cfg_id, device)
+    k, v = kv_inputs(cfg, cfg_id, device)
     return PrefillInputs(
         q_pre=normal((B, T, Hq, D), s("q_pre"), dt, device),
         qx_pre=normal((B, cfg.T_out, Hq, D), s("qx_pre"), dt, device),
-        k=normal((B, T, Hkv, D), s("k"), dt, device),
-        v=normal((B, T, Hkv, D), s("v"), dt, device),
-        alpha=a, beta=b, alpha_x=ax, beta_x=bx)
+        k=k, v=v, alpha=a, beta=b, alpha_x=ax, beta_x=bx)
 
 
 @dataclass
