@@ -1,0 +1,313 @@
+"""Benchmark of the Orthros attention hot path on one MI355X.
+
+One step = one pass over every part of the hot path on synthetic, seeded
+inputs already resident in HBM:
+  prefill_128k   cache append (T = 131072 rows), sliding-window prefill
+                 (W = 4096, query scale-offset fused), output-stream
+                 cross-attention at the last position (T_out = 1);
+                 B = 1, 32 query / 8 KV heads, D = 128, bf16
+  decode_pair    256 consecutive decode pair steps, B = 64 sequences with
+                 32768 cached tokens each (W = 2048); the cache length is
+                 rewound to 32768 at the start of every step
+The reported value is prefill tokens/s (B*T over the summed time of the
+three prefill launches); the decode pair's KV GB/s and latency, the full
+causal run at the same T (speedup ratio), the roofline of the dominant
+kernel and the fp64 CPU oracle's rate on a bounded sample are reported
+beside it. All GPU times come from HIP events on the launch stream.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-causal]
+                [--no-cpu-baseline] [--only prefill|decode]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Orthros prefill tokens/s @128K (SWA+global) + decode-pair KV GB/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+BAND_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
+                        "band_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def band_pairs(T, W):
+    """(query, key) pairs of the base stream per head: sum_t min(t+1, W)."""
+    W = min(W, T)
+    return W * (W + 1) // 2 + (T - W) * W
+
+
+def causal_pairs(T):
+    return T * (T + 1) // 2
+
+
+def kernel_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(name, sha):
+    """HBM bytes per launch of `name` from a committed counter summary, or
+    None if there is none or it was taken on other kernel source."""
+    path = os.path.join(PROFILES, f"{name}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sha:
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-causal", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
+              "is not supported (the attention path is run on one GPU's "
+              "share; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import long_context_prefill_swa_amd as lo
+    from workloads import (CONFIGS, affine_inputs, decode_all_steps,
+                           kv_inputs, prefill_inputs)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lo.lib()
+    stream = torch.cuda.current_stream(dev)
+    run_prefill = args.only in (None, "prefill")
+    run_decode = args.only in (None, "decode")
+
+    # ---- prefill_128k inputs ------------------------------------------------
+    pc = CONFIGS[4]
+    if run_prefill:
+        log(f"[bench] generating {pc.name} inputs")
+        px = prefill_inputs(pc, 4, dev)
+        kc4 = torch.empty((pc.B, pc.Hkv, pc.T, pc.D), dtype=torch.bfloat16,
+                          device=dev)
+        vc4 = torch.empty_like(kc4)
+        cl4 = torch.zeros(pc.B, dtype=torch.int32, device=dev)
+        o4 = torch.empty_like(px.q_pre)
+        ox4 = torch.empty_like(px.qx_pre)
+        ws4 = lo.workspace(lo.orthros_workspace_bytes(
+            lo.ORTHROS_OP_GLOBAL_XATTN, pc.B, pc.Hq, pc.Hkv, pc.D, pc.T_out,
+            pc.T), dev)
+
+    # ---- decode_pair inputs -----------------------------------------------
+    dc = CONFIGS[3]
+    n_dec = dc.decode_steps
+    if run_decode:
+        log(f"[bench] generating {dc.name} inputs")
+        cap3 = dc.T + n_dec
+        kc3 = torch.empty((dc.B, dc.Hkv, cap3, dc.D), dtype=torch.bfloat16,
+                          device=dev)
+        vc3 = torch.empty_like(kc3)
+        cl3 = torch.zeros(dc.B, dtype=torch.int32, device=dev)
+        k0, v0 = kv_inputs(dc, 3, dev)
+        lo.orthros_kv_append(kc3, vc3, cl3, k0, v0)
+        del k0, v0
+        a3, b3, ax3, bx3 = affine_inputs(dc, 3, dev)
+        st = decode_all_steps(dc, 3, device=dev)
+        o3 = torch.empty((dc.B, dc.Hq, dc.D), dtype=torch.bfloat16, device=dev)
+        ox3 = torch.empty_like(o3)
+        ws3 = lo.workspace(lo.orthros_workspace_bytes(
+            lo.ORTHROS_OP_DECODE_PAIR, dc.B, dc.Hq, dc.Hkv, dc.D, 1, cap3), dev)
+    torch.cuda.synchronize()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(record):
+        marks = {}
+        if run_prefill:
+            cl4.zero_()
+            marks["p0"] = ev()
+            lo.orthros_kv_append(kc4, vc4, cl4, px.k, px.v)
+            marks["p1"] = ev()
+            lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4,
+                                   pc.W)
+            marks["p2"] = ev()
+            lo.orthros_global_xattn(px.qx_pre, px.alpha_x, px.beta_x, kc4,
+                                    vc4, ox4, pc.T_in, ws=ws4)
+            marks["p3"] = ev()
+        if run_decode:
+            cl3.fill_(dc.T)
+            marks["d0"] = ev()
+            for s in range(n_dec):
+                lo.orthros_decode_pair(st.q_pre[s], st.qx_pre[s], a3, b3, ax3,
+                                       bx3, st.k_new[s], st.v_new[s], kc3,
+                                       vc3, cl3, o3, ox3, dc.T + s + 1, dc.W,
+                                       ws=ws3)
+            marks["d1"] = ev()
+        if record is not None:
+            record.append(marks)
+
+    log(f"[bench] warmup {args.warmup} step(s)")
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    lo.orthros_check_device_errors()
+
+    log(f"[bench] timing {args.steps} step(s)")
+    recs = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    start_ev = ev()
+    for _ in range(args.steps):
+        step(recs)
+    end_ev = ev()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    total_ms = start_ev.elapsed_time(end_ev)
+    lo.orthros_check_device_errors()
+    if run_decode:
+        assert cl3.tolist() == [dc.T + n_dec] * dc.B, "decode cache lengths"
+
+    def avg(a, b):
+        return sum(r[a].elapsed_time(r[b]) for r in recs) / len(recs)
+
+    out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": total_ms / args.steps, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "prefill_128k + decode_pair_b64",
+                      "prefill_128k": "B=1 Hq=32 Hkv=8 D=128 T=131072 W=4096 T_out=1",
+                      "decode_pair_b64": "B=64 Hq=32 Hkv=8 D=128 L0=32768 W=2048 steps=256",
+                      "global_batch": pc.B, "seq_len": pc.T}}
+    log(f"[bench] wall {wall:.2f}s, events {total_ms:.1f} ms")
+
+    if run_prefill:
+        t_app, t_swa, t_glob = avg("p0", "p1"), avg("p1", "p2"), avg("p2", "p3")
+        t_pre = t_app + t_swa + t_glob
+        F_swa = 4.0 * pc.D * band_pairs(pc.T, pc.W) * pc.Hq * pc.B
+        F_glob = 4.0 * pc.D * pc.T * pc.Hq * pc.B
+        kv_bytes = 2.0 * pc.B * pc.Hkv * pc.T * pc.D * 2
+        swa_tflops = F_swa / (t_swa * 1e-3) / 1e12
+        out["value"] = pc.B * pc.T / (t_pre * 1e-3)
+        out["prefill"] = {
+            "ms_kv_append": t_app, "ms_swa": t_swa, "ms_global": t_glob,
+            "ms_total": t_pre,
+            "attention_tflops": (F_swa + F_glob) / ((t_swa + t_glob) * 1e-3) / 1e12,
+            "attention_frac_of_bf16_peak":
+                (F_swa + F_glob) / ((t_swa + t_glob) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "swa_tflops": swa_tflops,
+            "global_GBps": kv_bytes / (t_glob * 1e-3) / 1e9,
+            "global_frac_of_hbm_peak": kv_bytes / (t_glob * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "kv_append_GBps": 2 * kv_bytes / (t_app * 1e-3) / 1e9,
+        }
+        sha = kernel_sha(BAND_SRC)
+        out["roofline"] = {
+            "kernel": "band_mfma_kernel (sliding-window prefill, prefill_128k)",
+            "bound": "mfma", "achieved": swa_tflops, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": swa_tflops / PEAK_BF16_TFLOPS,
+            "traffic": traffic_from_profile("band_mfma_prefill_128k", sha),
+            "algorithmic_flop_per_launch": F_swa,
+            "avg_launch_ms": t_swa, "kernel_source_sha256": sha}
+        log(f"[bench] prefill: append {t_app:.3f} ms, swa {t_swa:.3f} ms "
+            f"({swa_tflops:.1f} TFLOP/s), global {t_glob:.3f} ms")
+
+    if run_decode:
+        t_dec = avg("d0", "d1")
+        # algorithmic bytes per step: every cached K/V row read once per
+        # (sequence, KV head), plus the appended row, queries and outputs
+        L_sum = sum(dc.T + s + 1 for s in range(n_dec))
+        kv_read = 2.0 * dc.B * dc.Hkv * dc.D * 2 * L_sum
+        small = n_dec * dc.B * (4 * dc.Hq * dc.D * 2 + 2 * dc.Hkv * dc.D * 2)
+        gbps = (kv_read + small) / (t_dec * 1e-3) / 1e9
+        out["decode_pair"] = {
+            "ms_per_step": t_dec / n_dec, "ms_256_steps": t_dec,
+            "kv_GBps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS,
+            "algorithmic_bytes_256_steps": kv_read + small}
+        log(f"[bench] decode: {t_dec / n_dec:.3f} ms/step, {gbps:.0f} GB/s")
+        if not run_prefill:
+            out["value"] = None
+
+    # ---- full causal attention at the same T (speedup ratio) --------------
+    if run_prefill and not args.no_causal:
+        reps = 2
+        lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4, pc.T)
+        torch.cuda.synchronize()
+        e0 = ev()
+        for _ in range(reps):
+            lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4,
+                                   pc.T)
+        e1 = ev()
+        torch.cuda.synchronize()
+        t_c = e0.elapsed_time(e1) / reps
+        F_c = 4.0 * pc.D * causal_pairs(pc.T) * pc.Hq * pc.B
+        out["causal"] = {"ms": t_c, "tflops": F_c / (t_c * 1e-3) / 1e12,
+                         "speedup_vs_swa": t_c / out["prefill"]["ms_swa"]}
+        log(f"[bench] causal {t_c:.2f} ms, speedup {t_c / out['prefill']['ms_swa']:.1f}x")
+
+    # ---- CPU oracle on a bounded sample --------------------------------------
+    if run_prefill and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(px, pc)
+
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(px, pc, budget_s=12.0):
+    """The fp64 oracle on host cores, on a sample of the prefill_128k
+    workload: the output-stream row (all heads) once, then base-stream rows
+    (all heads) at evenly spread positions until `budget_s` is spent. The
+    rate is scaled to the full prefill (T base rows + one output row)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    log("[bench] cpu baseline: copying inputs")
+    k, v = f64(px.k), f64(px.v)
+    a, b, ax, bx = (f64(t) for t in (px.alpha, px.beta, px.alpha_x, px.beta_x))
+    t0 = time.perf_counter()
+    oracle.xattn(f64(px.qx_pre), ax, bx, k, v, pc.T_in)
+    t_glob = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    rows, t_rows = 0, 0.0
+    W = pc.W
+    while t_rows < budget_s and rows < 4096:
+        t = int(rng.integers(W, pc.T))
+        lo_t = t - W + 1
+        q = f64(px.q_pre[:, t:t + 1])
+        t0 = time.perf_counter()
+        oracle.xattn(q, a, b, k[:, lo_t:t + 1], v[:, lo_t:t + 1], t - lo_t)
+        t_rows += time.perf_counter() - t0
+        rows += 1
+    est = pc.T * (t_rows / rows) + t_glob
+    return {"value": pc.B * pc.T / est, "unit": "tokens/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": (f"prefill_128k: {rows} base-stream rows (W=4096, all 32 "
+                       f"heads) in {t_rows:.1f} s plus the output-stream row "
+                       f"(131072 keys, all heads) in {t_glob:.1f} s; scaled to "
+                       f"131072 base rows + 1 output row")}
+
+
+if __name__ == "__main__":
+    main()
