@@ -12,60 +12,70 @@
 // window as a local view rather than a masked T x T matrix. Here: key tiles
 // wholly outside a query tile's band are never loaded or multiplied.
 //
-// Tiling (one workgroup = 8 waves, 512 threads):
-//  * the workgroup owns 32*P consecutive query rows of the `gsize` query
-//    heads that share one KV head (P = 8 / gsize), so every K/V tile staged
-//    in LDS feeds 8 waves x 32 rows;
+// Tiling (one workgroup = NW waves):
+//  * the workgroup owns 32*NW/gsize consecutive query rows of the `gsize`
+//    query heads that share one KV head, so every K/V tile staged in LDS
+//    feeds NW waves x 32 rows;
 //  * wave w owns 32 rows of one query head; lane (j, h) = (lane % 32,
 //    lane / 32) holds query row j;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys on M, rows on N, D on K):
 //    each lane's 16 accumulators are 16 keys of its own row, so the row
 //    maximum needs one cross-lane exchange (lane j with lane j + 32);
 //  * O^T += V^T P^T on the same instruction (D on M, rows on N, keys on K):
-//    P^T comes straight from the S^T accumulators (no LDS round trip); V is
-//    written to LDS transposed, with the keys of every 16-key group permuted
-//    so that each lane reads its 8 keys with one 16-byte load;
+//    P^T comes straight from the S^T accumulators (no LDS round trip); V stays
+//    in LDS in its natural [key][d] layout and the V^T operand is read with
+//    the gfx950 transposing LDS load (ds_read_b64_tr_b16): within 16 lanes,
+//    lane i receives element i%4 of the 8-byte rows addressed by lanes
+//    4e + i/4 (e = 0..3), so pointing lane j at V[k0 + j/4][d0 + 4(j%4)]
+//    hands lane i the four keys k0..k0+3 of channel d0 + i;
 //  * the query is loaded once: affine in fp32, times log2(e)/sqrt(D), rounded
-//    to bf16; softmax runs in base 2 with exp2;
+//    to bf16; the softmax runs in base 2;
+//  * lazy rescaling: the running maximum m only moves when a tile's scores
+//    exceed it by more than 2^8 (then the accumulators are rescaled); the
+//    current -m is the accumulator input of the first S MFMA, so the scores
+//    arrive already shifted; exp2 arguments stay <= 8;
+//  * the row sum adds the same bf16 probabilities that feed the P V product
+//    (v_dot2_f32_bf16 against ones);
 //  * K/V tiles of 64 keys are double-buffered: the next tile's global loads
 //    are in flight while the current tile is multiplied;
 //  * workgroups are renumbered so that neighbouring query tiles of the same
 //    KV head run on the same XCD (shared L2 for the overlapping bands), and
 //    with an unbounded window the longest rows start first.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace orthros {
 namespace {
 
 constexpr int D = 128;
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kRows = 32;          // query rows per wave
 constexpr int kBN = 64;            // keys per LDS tile
-constexpr int kKS = D + 8;         // K tile row stride (bf16)
-constexpr int kVS = kBN + 8;       // V^T tile row stride (bf16)
+constexpr int kKS = D + 8;         // K tile row stride (bf16): 272 bytes
+constexpr int kVS = D + 16;        // V tile row stride (bf16): 288 bytes
+constexpr float kTau = 8.0f;       // lazy-rescale threshold (base-2 units)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct Smem {
   uint16_t k[2][kBN][kKS];
-  uint16_t vt[2][D][kVS];
+  uint16_t v[2][kBN][kVS];
 };
 
-// Position of key `e` (0..63) of a tile inside a V^T row: within every group
-// of 16 keys the quads are stored in the order 0, 2, 1, 3, so that lane half
-// h of the P^T operand (keys 4h..4h+3 and 8+4h..8+4h+3) reads 8 contiguous
-// entries.
-__device__ __forceinline__ int vt_slot(int e) {
-  const int q = (e >> 2) & 3;
-  const int perm = (q == 1) ? 2 : (q == 2) ? 1 : q;
-  return (e & ~15) + perm * 4 + (e & 3);
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
 }
 
-__global__ __launch_bounds__(kThreads, 1) void band_mfma_kernel(
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ alpha,
     const float *__restrict__ beta, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, uint16_t *__restrict__ o,
     int nrows, int Hq, int n_kv, int64_t cap, int64_t q_offset, int W,
     int n_qtiles, HeadGroups groups) {
+  constexpr int NT = NW * 64;
   __shared__ __attribute__((aligned(16))) Smem sm;
 
   // ---- workgroup -> (query tile, head group, batch) ------------------------
@@ -82,7 +92,7 @@ __global__ __launch_bounds__(kThreads, 1) void band_mfma_kernel(
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int j = lane & 31, hh = lane >> 5;
   const int gsize = groups.gsize;
-  const int P = kWaves / gsize;
+  const int P = NW / gsize;
   const int kvh = groups.kv[gi];
   const int head = groups.q[gi][w % gsize];
   const int ps = w / gsize;
@@ -123,62 +133,65 @@ __global__ __launch_bounds__(kThreads, 1) void band_mfma_kernel(
     for (int c = 0; c < 8; ++c) {
       const int d0 = 16 * c + 8 * hh;
       uint4 raw = make_uint4(0, 0, 0, 0);
-      if (act) raw = *(const uint4 *)(qp + d0);
+      float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+      if (act) {
+        raw = *(const uint4 *)(qp + d0);
+        a0 = *(const float4 *)(al + d0);
+        a1 = *(const float4 *)(al + d0 + 4);
+        b0 = *(const float4 *)(be + d0);
+        b1 = *(const float4 *)(be + d0 + 4);
+      }
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = 0.0f;
-        if (act) {
-          const float qv = bf16_bits_to_f32((e & 1) ? (wv[e >> 1] >> 16)
-                                                    : (wv[e >> 1] & 0xffffu));
-          x = (al[d0 + e] * qv + be[d0 + e]) * qs;
-        }
-        qop[c][e] = (__bf16)x;
+        const float qv = bf16_bits_to_f32((e & 1) ? (wv[e >> 1] >> 16)
+                                                  : (wv[e >> 1] & 0xffffu));
+        qop[c][e] = (__bf16)((av[e] * qv + bv[e]) * qs);
       }
     }
   }
 
-  // ---- tile staging: registers <-> LDS -------------------------------------
-  // K: thread loads rows (tid/16) and (tid/16 + 32), 16 bytes at 8*(tid%16).
-  // V: thread loads rows 2*(tid/16) and 2*(tid/16)+1 at the same channels and
-  //    writes them transposed as 8 key pairs.
-  const int st_row = tid >> 4, st_oct = tid & 15;
-  uint4 kreg[2], vreg[2];
+  // ---- tile staging: registers <-> LDS (16-byte chunks, natural layout) ----
+  constexpr int kChunks = kBN * D / 8 / NT;   // per thread, per tensor
+  uint4 kreg[kChunks], vreg[kChunks];
   auto load_tile = [&](int it) {
     const int64_t kb = (kt0 + it) * kBN;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t key = kb + st_row + 32 * i;
-      kreg[i] = (key <= k_hi) ? *(const uint4 *)(kc + key * D + 8 * st_oct)
-                              : make_uint4(0, 0, 0, 0);
-      const int64_t vkey = kb + 2 * st_row + i;
-      vreg[i] = (vkey <= k_hi) ? *(const uint4 *)(vc + vkey * D + 8 * st_oct)
-                               : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kChunks; ++i) {
+      const int idx = tid + NT * i;
+      const int64_t key = kb + (idx >> 4);
+      const int off = 8 * (idx & 15);
+      const bool ok = key <= k_hi;
+      kreg[i] = ok ? *(const uint4 *)(kc + key * D + off) : make_uint4(0, 0, 0, 0);
+      vreg[i] = ok ? *(const uint4 *)(vc + key * D + off) : make_uint4(0, 0, 0, 0);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *(uint4 *)&sm.k[buf][st_row + 32 * i][8 * st_oct] = kreg[i];
-    const uint32_t a0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-    const uint32_t a1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-    const int slot = vt_slot(2 * st_row);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // channel 8*oct + 2e: low halves; channel 8*oct + 2e + 1: high halves
-      const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
-      const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-      *(uint32_t *)&sm.vt[buf][8 * st_oct + 2 * e][slot] = lo;
-      *(uint32_t *)&sm.vt[buf][8 * st_oct + 2 * e + 1][slot] = hi;
+    for (int i = 0; i < kChunks; ++i) {
+      const int idx = tid + NT * i;
+      *(uint4 *)&sm.k[buf][idx >> 4][8 * (idx & 15)] = kreg[i];
+      *(uint4 *)&sm.v[buf][idx >> 4][8 * (idx & 15)] = vreg[i];
     }
   };
 
+  // Transposed-read addresses of the V^T operand: lane group g16 covers
+  // channels 16*(g16 % 2) (+32 dt) and key half hh = g16 / 2.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_row0 = 4 * hh + (j16 >> 2);          // + 16 kg (+ 8 second read)
+  const int v_col0 = 16 * (g16 & 1) + 4 * (j16 & 3);  // + 32 dt
+
   float m = -INFINITY, l = 0.0f;
-  f32x16 acc[4];
+  f32x16 acc[4], negm;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) negm[v] = 0.0f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   load_tile(0);
   store_tile(0);
@@ -191,12 +204,11 @@ __global__ __launch_bounds__(kThreads, 1) void band_mfma_kernel(
 
     const bool touch = wave_on && kb <= wk_hi && kb + kBN - 1 >= wk_lo;
     if (touch) {
-      // S^T for the two 32-key halves of the tile.
+      // S^T - m for the two 32-key halves of the tile.
       f32x16 s[2];
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[sk][v] = 0.0f;
+        s[sk] = negm;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const bf16x8 kop =
@@ -208,50 +220,61 @@ __global__ __launch_bounds__(kThreads, 1) void band_mfma_kernel(
       // Mask only tiles that cross a band edge of some row of this wave.
       const bool inside = (W <= 0 || kb >= wpos_hi - W + 1) &&
                           kb + kBN - 1 <= wpos_lo;
+      if (!inside) {
+#pragma unroll
+        for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t key = kb + 32 * sk + 8 * (v >> 2) + 4 * hh + (v & 3);
+            s[sk][v] = (key > tq || key < tq_lo) ? -INFINITY : s[sk][v];
+          }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (!inside) {
-            const int64_t key =
-                kb + 32 * sk + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (key > tq || key < tq_lo) s[sk][v] = -INFINITY;
-          }
-          tmax = fmaxf(tmax, s[sk][v]);
-        }
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[sk][v]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float m_new = fmaxf(m, tmax);
-      float corr = 1.0f;
-      bf16x8 pop[4];
-      if (m_new == -INFINITY) {
+      // Move the reference maximum only when needed (first keys of a row,
+      // or scores more than kTau above it).
+      const bool need = (m == -INFINITY) ? (tmax > -INFINITY) : (tmax > kTau);
+      if (__any(need)) {
+        const float shift = need ? tmax : 0.0f;
+        const float corr = need ? ((m == -INFINITY) ? 0.0f : exp2f(-shift)) : 1.0f;
+        m = need ? ((m == -INFINITY) ? shift : m + shift) : m;
+        l *= corr;
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg)
+        for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pop[kg][e] = (__bf16)0.0f;
-      } else {
-        corr = exp2f(m - m_new);
-        float ps_sum = 0.0f;
+        for (int sk = 0; sk < 2; ++sk) s[sk] -= shift;
+        const float nm = (m == -INFINITY) ? 0.0f : -m;
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const __bf16 pb = (__bf16)exp2f(s[kg >> 1][8 * (kg & 1) + e] - m_new);
-            pop[kg][e] = pb;
-            ps_sum += (float)pb;
-          }
-        l = l * corr + ps_sum;
+        for (int v = 0; v < 16; ++v) negm[v] = nm;
       }
-      m = m_new;
+      // P = exp2(S - m) in bf16; row sum of the same bf16 values.
+      bf16x8 pop[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
+      for (int kg = 0; kg < 4; ++kg) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pop[kg][e] = (__bf16)exp2f(s[kg >> 1][8 * (kg & 1) + e]);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pop[kg][e], pop[kg][e + 1]};
+          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        }
+      }
       // O^T += V^T P^T
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
-          const bf16x8 vop =
-              *(const bf16x8 *)&sm.vt[buf][32 * dt + j][16 * kg + 8 * hh];
+        for (int dt = 0; dt < 4; ++dt) {
+          const int row = 16 * kg + v_row0;
+          const int col = 32 * dt + v_col0;
+          const bf16x4 lo4 = lds_read_tr(&sm.v[buf][row][col]);
+          const bf16x4 hi4 = lds_read_tr(&sm.v[buf][row + 8][col]);
+          const bf16x8 vop = {lo4[0], lo4[1], lo4[2], lo4[3],
+                              hi4[0], hi4[1], hi4[2], hi4[3]};
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[kg],
                                                             acc[dt], 0, 0, 0);
         }
@@ -287,20 +310,34 @@ __global__ __launch_bounds__(kThreads, 1) void band_mfma_kernel(
 
 }  // namespace
 
+// Waves per workgroup: 8 (one workgroup per CU, widest K/V reuse) or 4 (two
+// independent workgroups per CU). Selected by ORTHROS_BAND_WAVES (default 8).
 hipError_t launch_band_mfma(const void *q, const float *alpha,
                             const float *beta, const void *k_cache,
                             const void *v_cache, void *o, int B, int nrows,
                             int Hq, int64_t cap, int64_t q_offset, int W,
                             const HeadGroups &groups, int n_kv,
                             hipStream_t stream) {
-  const int P = kWaves / groups.gsize;
+  static const int nw = [] {
+    const char *e = getenv("ORTHROS_BAND_WAVES");
+    return (e && atoi(e) == 4) ? 4 : 8;
+  }();
+  const int NW = (groups.gsize > 4) ? 8 : nw;
+  const int P = NW / groups.gsize;
   const int n_qtiles = (nrows + kRows * P - 1) / (kRows * P);
   const int64_t n_blocks = (int64_t)n_qtiles * groups.n_groups * B;
-  hipLaunchKernelGGL(band_mfma_kernel, dim3((unsigned)n_blocks),
-                     dim3(kThreads), 0, stream, (const uint16_t *)q, alpha,
-                     beta, (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                     (uint16_t *)o, nrows, Hq, n_kv, cap, q_offset, W,
-                     n_qtiles, groups);
+  if (NW == 8)
+    hipLaunchKernelGGL(band_mfma_kernel<8>, dim3((unsigned)n_blocks),
+                       dim3(512), 0, stream, (const uint16_t *)q, alpha, beta,
+                       (const uint16_t *)k_cache, (const uint16_t *)v_cache,
+                       (uint16_t *)o, nrows, Hq, n_kv, cap, q_offset, W,
+                       n_qtiles, groups);
+  else
+    hipLaunchKernelGGL(band_mfma_kernel<4>, dim3((unsigned)n_blocks),
+                       dim3(256), 0, stream, (const uint16_t *)q, alpha, beta,
+                       (const uint16_t *)k_cache, (const uint16_t *)v_cache,
+                       (uint16_t *)o, nrows, Hq, n_kv, cap, q_offset, W,
+                       n_qtiles, groups);
   return hipGetLastError();
 }
 

@@ -251,7 +251,7 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
       !tensor_elems(&n_elems, {B, T, Hq, D, 2}))
     return fail(ORTHROS_EINVAL, "tensor size overflows");
   hipError_t e;
-  if (mfma_eligible(dtype, D, {q_pre, k_cache, v_cache, o})) {
+  if (mfma_eligible(dtype, D, {q_pre, alpha, beta, k_cache, v_cache, o})) {
     e = launch_band_mfma(q_pre, alpha, beta, k_cache, v_cache, o, B, T, Hq,
                          cap, 0, W, groups, Hkv, as_stream(stream));
   } else {
@@ -291,7 +291,8 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
     return fail(ORTHROS_EINVAL, "tensor size overflows");
 
   hipError_t e;
-  const bool mfma = mfma_eligible(dtype, D, {qx_pre, k_cache, v_cache, o_x});
+  const bool mfma =
+      mfma_eligible(dtype, D, {qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x});
   const SplitPlan plan = plan_split(B, 1, T_out, groups, D, T);
   if (mfma && plan.use) {
     if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))
@@ -364,7 +365,8 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
 
   hipStream_t st = as_stream(stream);
   const bool mfma = mfma_eligible(
-      dtype, D, {q_pre, qx_pre, k_new, v_new, k_cache, v_cache, o, o_x});
+      dtype, D, {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new, v_new,
+                 k_cache, v_cache, o, o_x});
   const SplitPlan plan = plan_split(B, 2, 1, groups, D, max_len_after);
   if (mfma && plan.use && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)))
     return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
