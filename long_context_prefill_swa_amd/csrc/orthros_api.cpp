@@ -140,7 +140,9 @@ SplitPlan plan_split(int B, int n_streams, int n_pos, const HeadGroups &g,
                      int D, int64_t max_len) {
   SplitPlan p;
   p.rows = splitkv_rows(n_streams, n_pos, g.gsize);
-  if (D != 128 || p.rows > 16) return p;
+  // The split kernel addresses one (batch, KV head) slab of the cache with
+  // 32-bit byte offsets: max_len rows of 256 bytes must stay below 4 GiB.
+  if (D != 128 || p.rows > 16 || max_len > (int64_t)(UINT32_MAX / 256)) return p;
   p.use = true;
   p.chunk = splitkv_pick_chunk(B, g.n_groups, max_len);
   p.n_chunks = (int)((max_len + p.chunk - 1) / p.chunk);

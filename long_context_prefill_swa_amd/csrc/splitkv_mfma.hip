@@ -8,22 +8,34 @@
 //    base token's K/V, then the base query over its window and the output
 //    query over the whole cache.
 // Both stream every cache row once from HBM (§3.3: decoding is bound by
-// memory I/O), so the design goal is coalesced, deep-in-flight reads with
-// all query rows of a KV head sharing each read.
+// memory I/O), so the design goal is coalesced reads with many bytes in
+// flight and all query rows of a KV head sharing each read.
 //
 // Work split: grid (chunk, head group, batch). A workgroup (4 waves) owns
 // `chunk` consecutive keys of one (batch, KV head) and every query row that
 // reads that KV head (query heads of the group x streams x positions, at most
-// 16). Each wave takes 32 keys per step:
+// 16, one per MFMA column). The waves advance through the chunk 128 keys at a
+// time, wave w taking keys 32w..32w+31 of each 128; they never synchronise
+// inside the key loop. Per 32-key slice:
 //   S^T[key][row] = K Q^T        2 x 4 MFMA 16x16x32 (keys on M, rows on N)
 //   online softmax per row       (one row per lane column; no cross-row work)
 //   O^T[d][row] += V^T P^T        8 MFMA 16x16x32 (d on M, keys on K)
-// K is read straight from global memory into MFMA operand registers; V rows
-// are staged in LDS (a wave-private region) and gathered key-major for the
-// transposed product. Waves then merge in LDS and the workgroup writes one
+// K goes from global memory straight into MFMA operand registers. V rows are
+// written to a wave-private LDS region in their natural layout and the V^T
+// operand is read with the transposing LDS load (ds_read_b64_tr_b16). The
+// next slice's K and V are loaded into a second register set while the
+// current one is multiplied (two-stage pipeline, unrolled by two so both
+// sets stay in registers). All cache reads go through buffer resources whose
+// range ends at the workgroup's last valid key: reads past it return zeros
+// (never rows beyond the cache length), and the scores of those keys are
+// masked, so the loop has no data-dependent branch.
+//
+// After the loop the 4 waves merge in LDS and the workgroup writes one
 // (max, sum, unnormalised output) partial per row; a second kernel combines
-// the partials of all chunks with log-sum-exp weights, normalises, writes
-// the output rows and (decode) advances the cache length.
+// the partials of all chunks with log-sum-exp weights, normalises, writes the
+// output rows and (decode) advances the cache length.
+#include <cstdlib>
+
 #include "common.h"
 
 namespace orthros {
@@ -32,13 +44,39 @@ namespace {
 constexpr int D = 128;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStep = 32;           // keys per wave step
+constexpr int kSlice = 32;          // keys per wave per step
+constexpr int kStepKeys = kWaves * kSlice;
 constexpr int kMaxRows = 16;
-constexpr int kVStride = D + 8;     // bf16 elements per staged V row (pad)
+constexpr int kVS = D + 16;         // staged V row stride (bf16): 288 bytes
+constexpr int kAccS = D + 4;        // merge row stride (fp32)
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer access
 
-struct RowInfo {
-  int64_t lo, hi;  // key range, lo > hi = inactive
+struct VStage {
+  uint16_t v[kWaves][kSlice][kVS];  // 36 KB
 };
+struct Merge {
+  float acc[kWaves][kMaxRows][kAccS];  // 33 KB
+  float m[kWaves][kMaxRows];
+  float l[kWaves][kMaxRows];
+};
+union SplitSmem {
+  VStage st;
+  Merge mg;
+};
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
+
+// Orders this wave's LDS stores before its later LDS loads (other lanes of
+// the same wave read what a lane wrote). LDS operations of one wave execute
+// in order, so only the compiler has to be kept from reordering.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 __device__ __forceinline__ int64_t row_pos(const SplitKVArgs &a, int b,
                                            int j) {
@@ -52,13 +90,16 @@ __device__ __forceinline__ int64_t ws_part_index(const SplitKVArgs &a,
   return (((int64_t)b * n_groups + gi) * a.n_chunks + c) * rows + r;
 }
 
+// Registers of one 32-key slice: K in MFMA operand layout (lane (col, g4)
+// holds K[16 kt + col][32 c4 + 8 g4 ..]), V rows 4 i + g4 at channels 8 col.
+struct Slice {
+  uint4 k[2][4];
+  uint4 v[8];
+};
+
 __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
     SplitKVArgs a, HeadGroups groups) {
-  __shared__ __attribute__((aligned(16)))
-      uint16_t v_s[kWaves][kStep][kVStride];        // 17 KB
-  __shared__ float red_m[kWaves][kMaxRows];
-  __shared__ float red_l[kWaves][kMaxRows];
-  __shared__ float red_acc[kWaves][kMaxRows][D + 4];  // 33 KB
+  __shared__ __attribute__((aligned(16))) SplitSmem sm;
 
   const int c = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -81,45 +122,49 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   const int64_t hi_max = row_pos(a, b, a.n_pos - 1);
   const int64_t k_begin = (int64_t)c * a.chunk;
   if (k_begin > hi_max) return;
-  const int64_t k_end = k_begin + a.chunk;  // exclusive
+  // keys of this workgroup: [k_begin, k_stop)
+  const int64_t k_stop = min(k_begin + (int64_t)a.chunk, hi_max + 1);
+  const int n_steps = (int)((k_stop - k_begin + kStepKeys - 1) / kStepKeys);
 
-  // Per-row ranges (row = lane column `col` for this lane's softmax work).
-  RowInfo ri;
+  // This lane's softmax row (MFMA column `col`) and its key range.
   int row_h = -1, row_s = 0, row_j = 0;
   if (col < rows) {
     row_s = col / (a.n_pos * gsize);
     row_j = (col / gsize) % a.n_pos;
     row_h = groups.q[gi][col % gsize];
   }
+  int64_t r_lo = 1, r_hi = 0;  // empty unless the row is active
   if (row_h >= 0) {
     const int64_t t = row_pos(a, b, row_j);
-    const int Ws = a.W[row_s];
-    ri.lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
-    ri.hi = t;
-  } else {
-    ri.lo = 1;
-    ri.hi = 0;
+    const int Ws = row_s ? a.W[1] : a.W[0];
+    r_lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
+    r_hi = min(t, k_stop - 1);
   }
 
-  // cache pointers of this (batch, KV head)
-  const int64_t head_off =
-      ((int64_t)b * a.n_kv_heads + kvh) * a.cap * D;
-  const uint16_t *kc = (const uint16_t *)a.k_cache + head_off;
-  const uint16_t *vc = (const uint16_t *)a.v_cache + head_off;
-  const uint16_t *kn = nullptr, *vn = nullptr;
-  if (a.cache_len) {
-    kn = (const uint16_t *)a.k_new + ((int64_t)b * a.n_kv_heads + kvh) * D;
-    vn = (const uint16_t *)a.v_new + ((int64_t)b * a.n_kv_heads + kvh) * D;
-    // The workgroup whose chunk holds the new row also stores it.
-    if (n_old >= k_begin && n_old < k_end && w == 0 && lane < 32) {
+  // cache slab of this (batch, KV head); rows [0, k_stop) are readable
+  // through buffer resources, reads past them return zeros
+  const int64_t head_off = ((int64_t)b * a.n_kv_heads + kvh) * a.cap * D;
+  uint16_t *kc = (uint16_t *)a.k_cache + head_off;
+  uint16_t *vc = (uint16_t *)a.v_cache + head_off;
+  if (a.cache_len && n_old >= k_begin && n_old < k_stop) {
+    // Decode: this workgroup's chunk holds the new row. Store it first; it
+    // is the only workgroup that reads that row.
+    if (w == 0 && lane < 32) {
       const int part = lane & 15;
-      const uint4 *src = (const uint4 *)((lane < 16) ? kn : vn) + part;
-      uint4 *dst = (uint4 *)(((lane < 16) ? (uint16_t *)a.k_cache
-                                          : (uint16_t *)a.v_cache) +
-                             head_off + n_old * D) + part;
+      const int64_t src_off = ((int64_t)b * a.n_kv_heads + kvh) * D;
+      const uint4 *src = (const uint4 *)((const uint16_t *)((lane < 16) ? a.k_new : a.v_new) +
+                                         src_off) + part;
+      uint4 *dst = (uint4 *)(((lane < 16) ? kc : vc) + n_old * D) + part;
       *dst = *src;
     }
+    __threadfence();
+    __syncthreads();
   }
+  const uint32_t slab_bytes = (uint32_t)(k_stop * D * 2);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(kc, 0, slab_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(vc, 0, slab_bytes, kBufferWord3);
 
   // ---- query operand: Q^T (d on K, rows on N), affine + scale fused ------
   const float qscale = kLog2e * rsqrtf((float)D);
@@ -129,137 +174,154 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
     const uint16_t *qp = nullptr;
     const float *al = nullptr, *be = nullptr;
     if (act) {
-      qp = (const uint16_t *)a.q[row_s] +
+      qp = (const uint16_t *)(row_s ? a.q[1] : a.q[0]) +
            (((int64_t)b * a.n_pos + row_j) * a.Hq + row_h) * D;
-      al = a.alpha[row_s] + row_h * D;
-      be = a.beta[row_s] + row_h * D;
+      al = (row_s ? a.alpha[1] : a.alpha[0]) + row_h * D;
+      be = (row_s ? a.beta[1] : a.beta[0]) + row_h * D;
     }
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) {
       const int d0 = 32 * c4 + 8 * g4;
-      uint4 raw = act ? *(const uint4 *)(qp + d0) : make_uint4(0, 0, 0, 0);
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      float4 a0 = make_float4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
+      if (act) {
+        raw = *(const uint4 *)(qp + d0);
+        a0 = *(const float4 *)(al + d0);
+        a1 = *(const float4 *)(al + d0 + 4);
+        b0 = *(const float4 *)(be + d0);
+        b1 = *(const float4 *)(be + d0 + 4);
+      }
+      const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
       const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = 0.0f;
-        if (act) {
-          const float qv = bf16_bits_to_f32((e & 1) ? (wv[e >> 1] >> 16)
-                                                    : (wv[e >> 1] & 0xffffu));
-          x = (al[d0 + e] * qv + be[d0 + e]) * qscale;
-        }
-        qop[c4][e] = (__bf16)x;
+        const float qv = bf16_bits_to_f32((e & 1) ? (wv[e >> 1] >> 16)
+                                                  : (wv[e >> 1] & 0xffffu));
+        qop[c4][e] = (__bf16)((av[e] * qv + bv[e]) * qscale);
       }
     }
   }
+
+  // ---- slice loads ---------------------------------------------------------
+  // Slice `it` of this wave covers keys k_begin + 128 it + 32 w + [0, 32).
+  const uint32_t wave_off = (uint32_t)(kSlice * w) * (D * 2);
+  const uint32_t k_lane = (uint32_t)col * (D * 2) + 16u * g4;
+  const uint32_t v_lane = (uint32_t)g4 * (D * 2) + 16u * col;
+  auto load = [&](Slice &sl, int it) {
+    const uint32_t base = (uint32_t)(k_begin + (int64_t)it * kStepKeys) * (D * 2) + wave_off;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+        sl.k[kt][c4] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rk, base + k_lane + 16u * (D * 2) * kt + 64u * c4, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      sl.v[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rv, base + v_lane + 4u * (D * 2) * i, 0, 0));
+  };
+
+  // V^T transposed-read addresses: group g4 reads keys 4 g4.. (+16) and
+  // channels 16 dt + (lane % 16).
+  const int j16 = lane & 15;
+  uint16_t(*vs)[kVS] = sm.st.v[w];
+  const uint16_t *vtr0 = &vs[4 * g4 + (j16 >> 2)][4 * (j16 & 3)];
 
   float m = -INFINITY, l = 0.0f;
   f32x4 acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int n_steps = a.chunk / (kWaves * kStep);
-  for (int it = 0; it < n_steps; ++it) {
-    const int64_t key0 = k_begin + (int64_t)(it * kWaves + w) * kStep;
-
-    // K operand rows straight from global memory.
-    bf16x8 kop[2][4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int64_t key = key0 + 16 * kt + col;
-      const uint16_t *src = (a.cache_len && key == n_old) ? kn : kc + key * D;
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (key <= hi_max) raw = *(const uint4 *)(src + 32 * c4 + 8 * g4);
-        kop[kt][c4] = __builtin_bit_cast(bf16x8, raw);
-      }
-    }
-    // V rows into the wave's LDS region (16 lanes per 256-byte row).
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kr = 4 * i + g4;
-      const int64_t key = key0 + kr;
-      const uint16_t *src = (a.cache_len && key == n_old) ? vn : vc + key * D;
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (key <= hi_max) raw = *(const uint4 *)(src + 8 * col);
-      *(uint4 *)&v_s[w][kr][8 * col] = raw;
-    }
-
-    // S^T tiles.
+  auto compute = [&](const Slice &sl, int it) {
+    // S^T tiles: lane holds keys 16 kt + 4 g4 + i of row `col`.
     f32x4 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
-        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kt][c4], qop[c4],
-                                                        s[kt], 0, 0, 0);
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, sl.k[kt][c4]), qop[c4], s[kt], 0, 0,
+            0);
     }
+    // V rows into this wave's LDS region.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(uint4 *)&vs[4 * i + g4][8 * col] = sl.v[i];
 
     // Mask to the row's key range, online softmax (base-2 domain).
+    const int64_t kb = k_begin + (int64_t)it * kStepKeys + kSlice * w;
     float x[8];
     float tmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t key = key0 + 16 * kt + 4 * g4 + i;
-        const bool ok = key >= ri.lo && key <= ri.hi;
+        const int64_t key = kb + 16 * kt + 4 * g4 + i;
+        const bool ok = key >= r_lo && key <= r_hi;
         x[4 * kt + i] = ok ? s[kt][i] : -INFINITY;
         tmax = fmaxf(tmax, x[4 * kt + i]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m, tmax);
-    float corr = 1.0f;
+    const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float corr = exp2f(m - ms);  // 0 while the row has seen no key
     bf16x8 pop;
-    if (m_new == -INFINITY) {
+    float ps = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pop[e] = (__bf16)0.0f;
-    } else {
-      corr = exp2f(m - m_new);
-      float ps = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const __bf16 pb = (__bf16)exp2f(x[e] - m_new);
-        pop[e] = pb;
-        ps += (float)pb;
-      }
-      l = l * corr + ps;
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 pb = (__bf16)exp2f(x[e] - ms);
+      pop[e] = pb;
+      ps += (float)pb;
     }
+    l = l * corr + ps;
     m = m_new;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[dt] *= corr;
 
-    __syncthreads();  // V rows of every wave are in LDS
-    // O^T += V^T P^T: the P^T operand holds keys {4g4..4g4+3} of the first
-    // 16-key tile and the same of the second; V^T is gathered likewise.
+    wave_lds_fence();
+    // O^T += V^T P^T: P^T holds keys {4g4..4g4+3} and {16+4g4..} of row col.
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + col;
-      bf16x8 vop;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kr = (e < 4) ? (4 * g4 + e) : (16 + 4 * g4 + e - 4);
-        vop[e] = __builtin_bit_cast(__bf16, v_s[w][kr][d]);
-      }
+      const bf16x4 lo4 = lds_read_tr(vtr0 + 16 * dt);
+      const bf16x4 hi4 = lds_read_tr(vtr0 + 16 * kVS + 16 * dt);
+      const bf16x8 vop = {lo4[0], lo4[1], lo4[2], lo4[3],
+                          hi4[0], hi4[1], hi4[2], hi4[3]};
       acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[dt], 0,
                                                          0, 0);
     }
-    __syncthreads();  // LDS region free for the next step
+    wave_lds_fence();  // the next slice's stores come after these reads
+  };
+
+  // The scheduling barriers keep each prefetch ahead of the wait for the
+  // slice before it, so two slices are in flight while one is waited for.
+  Slice s0, s1;
+  load(s0, 0);
+  for (int it = 0; it < n_steps; it += 2) {
+    load(s1, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s0, it);
+    load(s0, it + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < n_steps) compute(s1, it + 1);
   }
 
   // ---- merge the 4 waves --------------------------------------------------
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
+  __syncthreads();  // every wave is done with its V region (union below)
   if (g4 == 0) {
-    red_m[w][col] = m;
-    red_l[w][col] = l;
+    sm.mg.m[w][col] = m;
+    sm.mg.l[w][col] = l;
   }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red_acc[w][col][16 * dt + 4 * g4 + i] = acc[dt][i];
+    for (int i = 0; i < 4; ++i)
+      sm.mg.acc[w][col][16 * dt + 4 * g4 + i] = acc[dt][i];
   __syncthreads();
 
   const int r = tid >> 4;          // 16 rows x 16 threads
@@ -267,16 +329,15 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   if (r < rows) {
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww][r]);
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.mg.m[ww][r]);
     float L = 0.0f, o8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (M != -INFINITY) {
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        const float mw = red_m[ww][r];
-        const float f = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-        L += f * red_l[ww][r];
+        const float f = exp2f(sm.mg.m[ww][r] - M);  // 0 for an empty wave
+        L += f * sm.mg.l[ww][r];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] += f * red_acc[ww][r][d0 + e];
+        for (int e = 0; e < 8; ++e) o8[e] += f * sm.mg.acc[ww][r][d0 + e];
       }
     }
     const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, c, r);
@@ -291,71 +352,96 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   }
 }
 
-// One block per (head group, batch); thread = (row, 8 channels).
+// One workgroup per (row, head group, batch). Thread (q, part): chunks
+// c_lo + q, c_lo + q + 16, ... and channels 8 part .. 8 part + 7; the 16
+// chunk lanes are then combined in LDS.
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
                                                             HeadGroups groups) {
-  const int gi = blockIdx.x, b = blockIdx.y;
+  __shared__ float sm_m[16], sm_l[16];
+  __shared__ float sm_acc[16][D + 4];
+  const int r = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int gsize = groups.gsize;
   const int rows = a.n_streams * a.n_pos * gsize;
+  const int s = r / (a.n_pos * gsize);
+  const int j = (r / gsize) % a.n_pos;
+  const int h = groups.q[gi][r % gsize];
   int64_t n_old = 0;
   bool ok = true;
   if (a.cache_len) {
     n_old = a.ws_len[b];
     ok = n_old >= 0;
   }
-  const int r = tid >> 4;
-  const int d0 = (tid & 15) * 8;
-  if (r < rows) {
-    const int s = r / (a.n_pos * gsize);
-    const int j = (r / gsize) % a.n_pos;
-    const int h = groups.q[gi][r % gsize];
-    if (h >= 0) {
-      uint16_t *out = (uint16_t *)a.o[s] +
-                      (((int64_t)b * a.n_pos + j) * a.Hq + h) * D + d0;
-      float o8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (ok) {
-        const int64_t t = (a.cache_len ? n_old : a.pos0) + j;
-        const int Ws = a.W[s];
-        const int64_t lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
-        const int c_lo = (int)(lo / a.chunk), c_hi = (int)(t / a.chunk);
-        float M = -INFINITY;
-        for (int c = c_lo; c <= c_hi; ++c) {
-          const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, c, r);
-          M = fmaxf(M, a.ws[pi * 2]);
-        }
-        float L = 0.0f;
-        for (int c = c_lo; c <= c_hi; ++c) {
-          const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, c, r);
-          const float mc = a.ws[pi * 2];
-          if (mc == -INFINITY) continue;
-          const float f = exp2f(mc - M);
-          L += f * a.ws[pi * 2 + 1];
-          const float *pacc = a.ws + (int64_t)a.ws_acc_offset + pi * D + d0;
-          const float4 u = *(const float4 *)pacc;
-          const float4 v = *(const float4 *)(pacc + 4);
-          o8[0] += f * u.x; o8[1] += f * u.y; o8[2] += f * u.z; o8[3] += f * u.w;
-          o8[4] += f * v.x; o8[5] += f * v.y; o8[6] += f * v.z; o8[7] += f * v.w;
-        }
-        const float inv = 1.0f / L;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] *= inv;
-      }
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo16 = __builtin_bit_cast(uint16_t, (__bf16)o8[2 * e]);
-        const uint32_t hi16 = __builtin_bit_cast(uint16_t, (__bf16)o8[2 * e + 1]);
-        pk[e] = lo16 | (hi16 << 16);
-      }
-      *(uint4 *)out = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    }
-  }
   // Decode: the cache now holds n_old + 1 rows for this batch entry. Every
   // split workgroup has finished reading (kernel boundary), and the merge
   // reads the old length from the workspace, so this write races with none.
-  if (a.cache_len && ok && gi == 0 && tid == 0)
+  // Row 0 of group 0 always exists (its first query head).
+  if (a.cache_len && ok && r == 0 && gi == 0 && tid == 0)
     ((int32_t *)a.cache_len)[b] = (int32_t)(n_old + 1);
+  if (h < 0) return;
+
+  const int q = tid >> 4, part = tid & 15, d0 = 8 * part;
+  float M = -INFINITY, L = 0.0f, o8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int64_t t = (a.cache_len ? n_old : a.pos0) + j;
+  int c_lo = 0, c_hi = -1;
+  if (ok) {
+    const int Ws = a.W[s];
+    const int64_t lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
+    c_lo = (int)(lo / a.chunk);
+    c_hi = (int)(t / a.chunk);
+  }
+  for (int cc = c_lo + q; cc <= c_hi; cc += 16) {
+    const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, cc, r);
+    const float mc = a.ws[pi * 2];
+    if (mc == -INFINITY) continue;
+    const float lc = a.ws[pi * 2 + 1];
+    const float *pacc = a.ws + (int64_t)a.ws_acc_offset + pi * D + d0;
+    const float4 u = *(const float4 *)pacc;
+    const float4 v = *(const float4 *)(pacc + 4);
+    const float Mn = fmaxf(M, mc);
+    const float fo = exp2f(M - Mn), fn = exp2f(mc - Mn);
+    L = L * fo + lc * fn;
+    const float pv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] = o8[e] * fo + pv[e] * fn;
+    M = Mn;
+  }
+  if (part == 0) {
+    sm_m[q] = M;
+    sm_l[q] = L;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm_acc[q][d0 + e] = o8[e];
+  __syncthreads();
+  if (tid < 16) {
+    // thread `part` = tid combines the 16 chunk lanes for channels 8 tid..
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) Mx = fmaxf(Mx, sm_m[qq]);
+    float Lx = 0.0f, out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int qq = 0; qq < 16; ++qq) {
+        const float f = exp2f(sm_m[qq] - Mx);
+        Lx += f * sm_l[qq];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] += f * sm_acc[qq][8 * tid + e];
+      }
+      const float inv = 1.0f / Lx;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] *= inv;
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo16 = __builtin_bit_cast(uint16_t, (__bf16)out[2 * e]);
+      const uint32_t hi16 = __builtin_bit_cast(uint16_t, (__bf16)out[2 * e + 1]);
+      pk[e] = lo16 | (hi16 << 16);
+    }
+    uint16_t *dst = (uint16_t *)a.o[s] +
+                    (((int64_t)b * a.n_pos + j) * a.Hq + h) * D + 8 * tid;
+    *(uint4 *)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
 }
 
 }  // namespace
@@ -364,10 +450,22 @@ int splitkv_rows(int n_streams, int n_pos, int gsize) {
   return n_streams * n_pos * gsize;
 }
 
+// Keys per workgroup: a power of two from 256 to 2048, the largest that still
+// gives every compute unit its two resident workgroups (gfx950 parts have 256
+// compute units). Long caches then run in whole rounds of long-lived
+// workgroups; short ones still spread over the whole chip. Depends on the
+// sizes only, so the workspace query needs no device.
 int splitkv_pick_chunk(int B, int n_groups, int64_t max_len) {
-  int chunk = 512;
-  while (chunk > 128 &&
-         (int64_t)B * n_groups * ((max_len + chunk - 1) / chunk) < 2048)
+  constexpr int64_t kResidentSlots = 2 * 256;
+  static const int max_chunk = [] {
+    const char *e = getenv("ORTHROS_SPLIT_CHUNK");
+    const int v = e ? atoi(e) : 0;
+    return (v == 256 || v == 512 || v == 1024 || v == 2048 || v == 4096) ? v
+                                                                         : 2048;
+  }();
+  int chunk = max_chunk;
+  while (chunk > 256 &&
+         (int64_t)B * n_groups * ((max_len + chunk - 1) / chunk) < kResidentSlots)
     chunk /= 2;
   return chunk;
 }
@@ -385,12 +483,13 @@ size_t splitkv_ws_bytes(int B, int n_groups, int rows, int n_chunks, int Dh) {
 hipError_t launch_splitkv(const SplitKVArgs &a_in, const HeadGroups &groups,
                           hipStream_t stream) {
   SplitKVArgs a = a_in;
+  const int rows = splitkv_rows(a.n_streams, a.n_pos, groups.gsize);
   dim3 grid(a.n_chunks, groups.n_groups, a.B);
   hipLaunchKernelGGL(splitkv_kernel, grid, dim3(kThreads), 0, stream, a,
                      groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(splitkv_merge_kernel, dim3(groups.n_groups, a.B),
+  hipLaunchKernelGGL(splitkv_merge_kernel, dim3(rows, groups.n_groups, a.B),
                      dim3(256), 0, stream, a, groups);
   return hipGetLastError();
 }
