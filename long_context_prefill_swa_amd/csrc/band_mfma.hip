@@ -52,7 +52,8 @@ constexpr int D = 128;
 constexpr int kRows = 32;          // query rows per wave
 constexpr int kBN = 64;            // keys per LDS tile
 constexpr int kKS = D + 8;         // K tile row stride (bf16): 272 bytes
-constexpr int kVS = D + 16;        // V tile row stride (bf16): 288 bytes
+constexpr int kVS = D + 32;        // V tile row stride (bf16): 320 bytes
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped) buffer access
 constexpr float kTau = 8.0f;       // lazy-rescale threshold (base-2 units)
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -115,11 +116,17 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
   const int64_t wk_hi = wpos_hi;
   const int rq = wr0 + j;                      // this lane's query row
   const int64_t tq = q_offset + rq;
-  const int64_t tq_lo = (W > 0) ? tq - W + 1 : INT64_MIN;
+  // Band of this lane's row in offsets d = key - tq: -Wm < d <= 0.
+  const int Wm = (W > 0) ? W : INT32_MAX;
 
+  // Cache slab of this (batch, KV head), read through buffer resources that
+  // end after key k_hi: tile rows past it load as zeros.
   const int64_t head_off = ((int64_t)b * n_kv + kvh) * cap * D;
-  const uint16_t *kc = k_cache + head_off;
-  const uint16_t *vc = v_cache + head_off;
+  const uint32_t slab_bytes = (uint32_t)((k_hi + 1) * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(k_cache + head_off), 0, slab_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(v_cache + head_off), 0, slab_bytes, kBufferWord3);
 
   // ---- query operand (B of S^T): rows on N, D on K ------------------------
   bf16x8 qop[8];
@@ -157,15 +164,14 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
   constexpr int kChunks = kBN * D / 8 / NT;   // per thread, per tensor
   uint4 kreg[kChunks], vreg[kChunks];
   auto load_tile = [&](int it) {
-    const int64_t kb = (kt0 + it) * kBN;
+    const uint32_t tile_off = (uint32_t)((kt0 + it) * kBN) * (D * 2);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const int idx = tid + NT * i;
-      const int64_t key = kb + (idx >> 4);
-      const int off = 8 * (idx & 15);
-      const bool ok = key <= k_hi;
-      kreg[i] = ok ? *(const uint4 *)(kc + key * D + off) : make_uint4(0, 0, 0, 0);
-      vreg[i] = ok ? *(const uint4 *)(vc + key * D + off) : make_uint4(0, 0, 0, 0);
+      const uint32_t off = tile_off + 16u * (uint32_t)(tid + NT * i);
+      kreg[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vreg[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
     }
   };
   auto store_tile = [&](int buf) {
@@ -221,12 +227,13 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
       const bool inside = (W <= 0 || kb >= wpos_hi - W + 1) &&
                           kb + kBN - 1 <= wpos_lo;
       if (!inside) {
+        const int d0 = (int)(kb - tq);  // |kb - tq| < 2^31 (cap < 2^31)
 #pragma unroll
         for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int64_t key = kb + 32 * sk + 8 * (v >> 2) + 4 * hh + (v & 3);
-            s[sk][v] = (key > tq || key < tq_lo) ? -INFINITY : s[sk][v];
+            const int d = d0 + 32 * sk + 8 * (v >> 2) + 4 * hh + (v & 3);
+            s[sk][v] = (d > 0 || d <= -Wm) ? -INFINITY : s[sk][v];
           }
       }
       float tmax = -INFINITY;
@@ -234,13 +241,13 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
       for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
         for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[sk][v]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = max_xor32(tmax);
       // Move the reference maximum only when needed (first keys of a row,
       // or scores more than kTau above it).
       const bool need = (m == -INFINITY) ? (tmax > -INFINITY) : (tmax > kTau);
       if (__any(need)) {
         const float shift = need ? tmax : 0.0f;
-        const float corr = need ? ((m == -INFINITY) ? 0.0f : exp2f(-shift)) : 1.0f;
+        const float corr = need ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(-shift)) : 1.0f;
         m = need ? ((m == -INFINITY) ? shift : m + shift) : m;
         l *= corr;
 #pragma unroll
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
       for (int kg = 0; kg < 4; ++kg) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pop[kg][e] = (__bf16)exp2f(s[kg >> 1][8 * (kg & 1) + e]);
+          pop[kg][e] = (__bf16)__builtin_amdgcn_exp2f(s[kg >> 1][8 * (kg & 1) + e]);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pr = {pop[kg][e], pop[kg][e + 1]};

@@ -37,6 +37,16 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// max(v, v of lane ^ 32), one v_permlane32_swap (gfx950) instead of an LDS
+// permute: swapping the upper half of one copy with the lower half of
+// another leaves each lane holding both values of its pair.
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v),
+                                                  __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ---- launchers (defined in the .hip files) --------------------------------
 
 // Sticky device error flag (capacity faults); address on the current device.

@@ -120,8 +120,13 @@ bool tensor_elems(int64_t *out, std::initializer_list<int64_t> dims) {
   return true;
 }
 
-bool mfma_eligible(int dtype, int D, std::initializer_list<const void *> ptrs) {
+// MFMA kernels: bf16, D = 128, 16-byte aligned tensors, and key ranges whose
+// byte offsets inside one (batch, KV head) slab fit 32 bits (n_keys rows of
+// 256 bytes), as the kernels address the cache through buffer resources.
+bool mfma_eligible(int dtype, int D, int64_t n_keys,
+                   std::initializer_list<const void *> ptrs) {
   if (dtype != ORTHROS_BF16 || D != 128) return false;
+  if (n_keys > (int64_t)(UINT32_MAX / 256)) return false;
   for (const void *p : ptrs)
     if (!aligned16(p)) return false;
   return true;
@@ -253,7 +258,7 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
       !tensor_elems(&n_elems, {B, T, Hq, D, 2}))
     return fail(ORTHROS_EINVAL, "tensor size overflows");
   hipError_t e;
-  if (mfma_eligible(dtype, D, {q_pre, alpha, beta, k_cache, v_cache, o})) {
+  if (mfma_eligible(dtype, D, T, {q_pre, alpha, beta, k_cache, v_cache, o})) {
     e = launch_band_mfma(q_pre, alpha, beta, k_cache, v_cache, o, B, T, Hq,
                          cap, 0, W, groups, Hkv, as_stream(stream));
   } else {
@@ -294,7 +299,7 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
 
   hipError_t e;
   const bool mfma =
-      mfma_eligible(dtype, D, {qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x});
+      mfma_eligible(dtype, D, T, {qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x});
   const SplitPlan plan = plan_split(B, 1, T_out, groups, D, T);
   if (mfma && plan.use) {
     if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))
@@ -367,7 +372,7 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
 
   hipStream_t st = as_stream(stream);
   const bool mfma = mfma_eligible(
-      dtype, D, {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new, v_new,
+      dtype, D, max_len_after, {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new, v_new,
                  k_cache, v_cache, o, o_x});
   const SplitPlan plan = plan_split(B, 2, 1, groups, D, max_len_after);
   if (mfma && plan.use && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)))

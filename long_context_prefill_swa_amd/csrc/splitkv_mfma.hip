@@ -268,12 +268,12 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m, tmax);
     const float ms = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float corr = exp2f(m - ms);  // 0 while the row has seen no key
+    const float corr = __builtin_amdgcn_exp2f(m - ms);  // 0 while the row has seen no key
     bf16x8 pop;
     float ps = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const __bf16 pb = (__bf16)exp2f(x[e] - ms);
+      const __bf16 pb = (__bf16)__builtin_amdgcn_exp2f(x[e] - ms);
       pop[e] = pb;
       ps += (float)pb;
     }
