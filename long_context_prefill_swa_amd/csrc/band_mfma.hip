@@ -112,8 +112,6 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
   const bool wave_on = head >= 0 && wr0 < nrows;
   const int64_t wpos_lo = q_offset + wr0;
   const int64_t wpos_hi = q_offset + min(wr0 + kRows, nrows) - 1;
-  const int64_t wk_lo = (W > 0) ? max((int64_t)0, wpos_lo - W + 1) : 0;
-  const int64_t wk_hi = wpos_hi;
   const int rq = wr0 + j;                      // this lane's query row
   const int64_t tq = q_offset + rq;
   // Band of this lane's row in offsets d = key - tq: -Wm < d <= 0.
@@ -163,26 +161,35 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
   // ---- tile staging: registers <-> LDS (16-byte chunks, natural layout) ----
   constexpr int kChunks = kBN * D / 8 / NT;   // per thread, per tensor
   uint4 kreg[kChunks], vreg[kChunks];
-  auto load_tile = [&](int it) {
-    const uint32_t tile_off = (uint32_t)((kt0 + it) * kBN) * (D * 2);
+  // Staging registers: K of one tile and V of the tile before it.
+  auto load_tile = [&](int kt) {
+    const uint32_t k_off = (uint32_t)((kt0 + kt) * kBN) * (D * 2);
+    const uint32_t v_off = k_off - (uint32_t)(kBN * D * 2);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const uint32_t off = tile_off + 16u * (uint32_t)(tid + NT * i);
+      const uint32_t off = 16u * (uint32_t)(tid + NT * i);
       kreg[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-      vreg[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + off, 0, 0));
+      if (kt > 0)
+        vreg[i] = __builtin_bit_cast(
+            uint4,
+            __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + off, 0, 0));
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int idx = tid + NT * i;
       *(uint4 *)&sm.k[buf][idx >> 4][8 * (idx & 15)] = kreg[i];
+    }
+  };
+  auto store_v_next = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int idx = tid + NT * i;
       *(uint4 *)&sm.v[buf][idx >> 4][8 * (idx & 15)] = vreg[i];
     }
   };
-
   // Transposed-read addresses of the V^T operand: lane group g16 covers
   // channels 16*(g16 % 2) (+32 dt) and key half hh = g16 / 2.
   const int g16 = lane >> 4, j16 = lane & 15;
@@ -199,97 +206,138 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
   for (int v = 0; v < 16; ++v) negm[v] = 0.0f;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int64_t kb = (kt0 + it) * kBN;
-    if (it + 1 < ntiles) load_tile(it + 1);
-
-    const bool touch = wave_on && kb <= wk_hi && kb + kBN - 1 >= wk_lo;
-    if (touch) {
-      // S^T - m for the two 32-key halves of the tile.
-      f32x16 s[2];
+  // S^T - m of one tile: keys of K buffer `kbuf`, seeded with the current -m.
+  auto scores = [&](f32x16 (&sn)[2], int kbuf) {
+    sn[0] = negm;
+    sn[1] = negm;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk) {
-        s[sk] = negm;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const bf16x8 kop =
-              *(const bf16x8 *)&sm.k[buf][32 * sk + j][16 * c + 8 * hh];
-          s[sk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[c], s[sk],
-                                                          0, 0, 0);
-        }
+        const bf16x8 kop =
+            *(const bf16x8 *)&sm.k[kbuf][32 * sk + j][16 * c + 8 * hh];
+        sn[sk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[c], sn[sk],
+                                                         0, 0, 0);
       }
-      // Mask only tiles that cross a band edge of some row of this wave.
-      const bool inside = (W <= 0 || kb >= wpos_hi - W + 1) &&
-                          kb + kBN - 1 <= wpos_lo;
-      if (!inside) {
-        const int d0 = (int)(kb - tq);  // |kb - tq| < 2^31 (cap < 2^31)
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int d = d0 + 32 * sk + 8 * (v >> 2) + 4 * hh + (v & 3);
-            s[sk][v] = (d > 0 || d <= -Wm) ? -INFINITY : s[sk][v];
-          }
-      }
-      float tmax = -INFINITY;
+  };
+  // Band mask (only tiles crossing a band edge of some row of this wave),
+  // row maximum, and the lazy move of the reference maximum.
+  auto settle = [&](f32x16 (&sn)[2], int64_t kb) {
+    const bool inside = (W <= 0 || kb >= wpos_hi - W + 1) &&
+                        kb + kBN - 1 <= wpos_lo;
+    if (!inside) {
+      const int d0 = (int)(kb - tq);  // |kb - tq| < 2^31 (cap < 2^31)
 #pragma unroll
       for (int sk = 0; sk < 2; ++sk)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[sk][v]);
-      tmax = max_xor32(tmax);
-      // Move the reference maximum only when needed (first keys of a row,
-      // or scores more than kTau above it).
-      const bool need = (m == -INFINITY) ? (tmax > -INFINITY) : (tmax > kTau);
-      if (__any(need)) {
-        const float shift = need ? tmax : 0.0f;
-        const float corr = need ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(-shift)) : 1.0f;
-        m = need ? ((m == -INFINITY) ? shift : m + shift) : m;
-        l *= corr;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk) s[sk] -= shift;
-        const float nm = (m == -INFINITY) ? 0.0f : -m;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) negm[v] = nm;
-      }
-      // P = exp2(S - m) in bf16; row sum of the same bf16 values.
-      bf16x8 pop[4];
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pop[kg][e] = (__bf16)__builtin_amdgcn_exp2f(s[kg >> 1][8 * (kg & 1) + e]);
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pop[kg][e], pop[kg][e + 1]};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
-        }
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int row = 16 * kg + v_row0;
-          const int col = 32 * dt + v_col0;
-          const bf16x4 lo4 = lds_read_tr(&sm.v[buf][row][col]);
-          const bf16x4 hi4 = lds_read_tr(&sm.v[buf][row + 8][col]);
-          const bf16x8 vop = {lo4[0], lo4[1], lo4[2], lo4[3],
-                              hi4[0], hi4[1], hi4[2], hi4[3]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[kg],
-                                                            acc[dt], 0, 0, 0);
+        for (int v = 0; v < 16; ++v) {
+          const int d = d0 + 32 * sk + 8 * (v >> 2) + 4 * hh + (v & 3);
+          sn[sk][v] = (d > 0 || d <= -Wm) ? -INFINITY : sn[sk][v];
         }
     }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sk = 0; sk < 2; ++sk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sn[sk][v]);
+    tmax = max_xor32(tmax);
+    // Move the reference maximum only when needed (first keys of a row, or
+    // scores more than kTau above it).
+    const bool need = (m == -INFINITY) ? (tmax > -INFINITY) : (tmax > kTau);
+    if (__any(need)) {
+      const float shift = need ? tmax : 0.0f;
+      const float corr =
+          need ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(-shift))
+               : 1.0f;
+      m = need ? ((m == -INFINITY) ? shift : m + shift) : m;
+      l *= corr;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
+#pragma unroll
+      for (int sk = 0; sk < 2; ++sk) sn[sk] -= shift;
+      const float nm = (m == -INFINITY) ? 0.0f : -m;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) negm[v] = nm;
+    }
+  };
 
-    if (it + 1 < ntiles) store_tile(buf ^ 1);
+  // Software pipeline, one 64-key tile per step. Entering step `it`:
+  // scores of tile it are settled in registers, K of tile it+1 and V of tile
+  // it are in LDS, K of tile it+2 and V of tile it+1 are being loaded. The
+  // step multiplies the next tile's scores while it exponentiates this one
+  // (MFMA and VALU work of one wave overlap), then accumulates P V and
+  // settles the next scores. Tiles past the last one load as zeros and are
+  // masked, so the pipeline needs no tail branch.
+  load_tile(0);
+  store_k(0);
+  load_tile(1);
+  store_k(1);
+  store_v_next(0);
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  scores(sa, 0);
+  settle(sa, kt0 * kBN);
+  __syncthreads();  // K buffer 0 is refilled at the end of step 0
+
+  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int it) {
+    const int64_t kb = (kt0 + it) * kBN;
+    load_tile(it + 2);  // K of tile it+2, V of tile it+1 (see store below)
+    scores(sn, (it + 1) & 1);
+    bf16x8 pop[4];
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pop[kg][e] =
+            (__bf16)__builtin_amdgcn_exp2f(sc[kg >> 1][8 * (kg & 1) + e]);
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 pr = {pop[kg][e], pop[kg][e + 1]};
+        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+      }
+    }
+    // O^T += V^T P^T
+    const int vb = it & 1;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int row = 16 * kg + v_row0;
+        const int col = 32 * dt + v_col0;
+        const bf16x4 lo4 = lds_read_tr(&sm.v[vb][row][col]);
+        const bf16x4 hi4 = lds_read_tr(&sm.v[vb][row + 8][col]);
+        const bf16x8 vop = {lo4[0], lo4[1], lo4[2], lo4[3],
+                            hi4[0], hi4[1], hi4[2], hi4[3]};
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[kg],
+                                                          acc[dt], 0, 0, 0);
+      }
+    // Instruction order for the block above: the next tile's score MFMAs
+    // interleaved with this tile's exponentials, conversions and row-sum
+    // dots, then the P V MFMAs; LDS operand reads run two MFMAs ahead.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // K operand reads
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // score MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // K reads, then V^T
+      __builtin_amdgcn_sched_group_barrier(0x400, 4, 0);  // exp2
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // cvt, dot2
+    }
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V^T reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V MFMA
+    }
+    settle(sn, kb + kBN);
+    store_k(it & 1);
+    store_v_next(vb ^ 1);
     __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    step(sa, sb, it);
+    step(sb, sa, it + 1);
   }
+  if (it < ntiles) step(sa, sb, it);
 
   // ---- epilogue: normalise and store ---------------------------------------
   l += __shfl_xor(l, 32, 64);
