@@ -41,7 +41,6 @@
 //  * workgroups are renumbered so that neighbouring query tiles of the same
 //    KV head run on the same XCD (shared L2 for the overlapping bands), and
 //    with an unbounded window the longest rows start first.
-#include <cstdlib>
 
 #include "common.h"
 
@@ -160,34 +159,36 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
 
   // ---- tile staging: registers <-> LDS (16-byte chunks, natural layout) ----
   constexpr int kChunks = kBN * D / 8 / NT;   // per thread, per tensor
-  uint4 kreg[kChunks], vreg[kChunks];
-  // Staging registers: K of one tile and V of the tile before it.
-  auto load_tile = [&](int kt) {
+  // A staging set holds K of one tile and V of the tile before it.
+  struct Stage {
+    uint4 k[kChunks], v[kChunks];
+  };
+  auto load_tile = [&](Stage &r, int kt) {
     const uint32_t k_off = (uint32_t)((kt0 + kt) * kBN) * (D * 2);
     const uint32_t v_off = k_off - (uint32_t)(kBN * D * 2);
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const uint32_t off = 16u * (uint32_t)(tid + NT * i);
-      kreg[i] = __builtin_bit_cast(
+      r.k[i] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + off, 0, 0));
       if (kt > 0)
-        vreg[i] = __builtin_bit_cast(
+        r.v[i] = __builtin_bit_cast(
             uint4,
             __builtin_amdgcn_raw_buffer_load_b128(rv, v_off + off, 0, 0));
     }
   };
-  auto store_k = [&](int buf) {
+  auto store_k = [&](const Stage &r, int buf) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int idx = tid + NT * i;
-      *(uint4 *)&sm.k[buf][idx >> 4][8 * (idx & 15)] = kreg[i];
+      *(uint4 *)&sm.k[buf][idx >> 4][8 * (idx & 15)] = r.k[i];
     }
   };
-  auto store_v_next = [&](int buf) {
+  auto store_v = [&](const Stage &r, int buf) {
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int idx = tid + NT * i;
-      *(uint4 *)&sm.v[buf][idx >> 4][8 * (idx & 15)] = vreg[i];
+      *(uint4 *)&sm.v[buf][idx >> 4][8 * (idx & 15)] = r.v[i];
     }
   };
   // Transposed-read addresses of the V^T operand: lane group g16 covers
@@ -263,25 +264,32 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
 
   // Software pipeline, one 64-key tile per step. Entering step `it`:
   // scores of tile it are settled in registers, K of tile it+1 and V of tile
-  // it are in LDS, K of tile it+2 and V of tile it+1 are being loaded. The
-  // step multiplies the next tile's scores while it exponentiates this one
-  // (MFMA and VALU work of one wave overlap), then accumulates P V and
-  // settles the next scores. Tiles past the last one load as zeros and are
+  // it are in LDS, and K of tile it+2 with V of tile it+1 are arriving in one
+  // staging set (loaded during the previous step). The step starts the loads
+  // of K of tile it+3 and V of tile it+2 into the other set, multiplies the
+  // next tile's scores while it exponentiates this one (MFMA and VALU work of
+  // one wave overlap), accumulates P V, settles the next scores and moves
+  // the arrived set into LDS. Tiles past the last one load as zeros and are
   // masked, so the pipeline needs no tail branch.
-  load_tile(0);
-  store_k(0);
-  load_tile(1);
-  store_k(1);
-  store_v_next(0);
+  // Prologue: K of tiles 0 and 1 and V of tile 0 are loaded together, then
+  // stored; K of tile 2 and V of tile 1 stay in flight through step 0.
+  Stage ra, rb;
+  load_tile(rb, 0);
+  load_tile(ra, 1);
+  store_k(rb, 0);
+  store_k(ra, 1);
+  store_v(ra, 0);
+  load_tile(ra, 2);
   __syncthreads();
   f32x16 sa[2], sb[2];
   scores(sa, 0);
   settle(sa, kt0 * kBN);
   __syncthreads();  // K buffer 0 is refilled at the end of step 0
 
-  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int it) {
+  auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], Stage &r_in,
+                  Stage &r_out, int it) {
     const int64_t kb = (kt0 + it) * kBN;
-    load_tile(it + 2);  // K of tile it+2, V of tile it+1 (see store below)
+    load_tile(r_out, it + 3);  // stored at the end of the next step
     scores(sn, (it + 1) & 1);
     bf16x8 pop[4];
 #pragma unroll
@@ -328,16 +336,16 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V MFMA
     }
     settle(sn, kb + kBN);
-    store_k(it & 1);
-    store_v_next(vb ^ 1);
+    store_k(r_in, it & 1);     // K of tile it+2
+    store_v(r_in, vb ^ 1);     // V of tile it+1
     __syncthreads();
   };
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
-    step(sa, sb, it);
-    step(sb, sa, it + 1);
+    step(sa, sb, ra, rb, it);
+    step(sb, sa, rb, ra, it + 1);
   }
-  if (it < ntiles) step(sa, sb, it);
+  if (it < ntiles) step(sa, sb, ra, rb, it);
 
   // ---- epilogue: normalise and store ---------------------------------------
   l += __shfl_xor(l, 32, 64);
@@ -365,34 +373,21 @@ __global__ __launch_bounds__(NW * 64, 2) void band_mfma_kernel(
 
 }  // namespace
 
-// Waves per workgroup: 8 (one workgroup per CU, widest K/V reuse) or 4 (two
-// independent workgroups per CU). Selected by ORTHROS_BAND_WAVES (default 8).
 hipError_t launch_band_mfma(const void *q, const float *alpha,
                             const float *beta, const void *k_cache,
                             const void *v_cache, void *o, int B, int nrows,
                             int Hq, int64_t cap, int64_t q_offset, int W,
                             const HeadGroups &groups, int n_kv,
                             hipStream_t stream) {
-  static const int nw = [] {
-    const char *e = getenv("ORTHROS_BAND_WAVES");
-    return (e && atoi(e) == 4) ? 4 : 8;
-  }();
-  const int NW = (groups.gsize > 4) ? 8 : nw;
+  constexpr int NW = 8;  // one workgroup per compute unit
   const int P = NW / groups.gsize;
   const int n_qtiles = (nrows + kRows * P - 1) / (kRows * P);
   const int64_t n_blocks = (int64_t)n_qtiles * groups.n_groups * B;
-  if (NW == 8)
-    hipLaunchKernelGGL(band_mfma_kernel<8>, dim3((unsigned)n_blocks),
-                       dim3(512), 0, stream, (const uint16_t *)q, alpha, beta,
-                       (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                       (uint16_t *)o, nrows, Hq, n_kv, cap, q_offset, W,
-                       n_qtiles, groups);
-  else
-    hipLaunchKernelGGL(band_mfma_kernel<4>, dim3((unsigned)n_blocks),
-                       dim3(256), 0, stream, (const uint16_t *)q, alpha, beta,
-                       (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                       (uint16_t *)o, nrows, Hq, n_kv, cap, q_offset, W,
-                       n_qtiles, groups);
+  hipLaunchKernelGGL(band_mfma_kernel<NW>, dim3((unsigned)n_blocks),
+                     dim3(NW * 64), 0, stream, (const uint16_t *)q, alpha,
+                     beta, (const uint16_t *)k_cache,
+                     (const uint16_t *)v_cache, (uint16_t *)o, nrows, Hq,
+                     n_kv, cap, q_offset, W, n_qtiles, groups);
   return hipGetLastError();
 }
 
