@@ -36,6 +36,8 @@ PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 BAND_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
                         "band_mfma.hip")
+SPLIT_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
+                         "splitkv_mfma.hip")
 
 
 def log(*a):
@@ -242,6 +244,17 @@ def main():
             "ms_per_step": t_dec / n_dec, "ms_256_steps": t_dec,
             "kv_GBps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS,
             "algorithmic_bytes_256_steps": kv_read + small}
+        # The decode pair's dominant kernel is the split-KV stream; its
+        # launch is bracketed together with the short merge kernel.
+        sha_s = kernel_sha(SPLIT_SRC)
+        step_bytes = (kv_read + small) / n_dec
+        out["roofline_decode"] = {
+            "kernel": "splitkv_kernel + splitkv_merge_kernel (decode pair step, B=64)",
+            "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
+            "traffic": traffic_from_profile("splitkv_decode_b64", sha_s),
+            "algorithmic_bytes_per_launch": step_bytes,
+            "avg_launch_ms": t_dec / n_dec, "kernel_source_sha256": sha_s}
         log(f"[bench] decode: {t_dec / n_dec:.3f} ms/step, {gbps:.0f} GB/s")
         if not run_prefill:
             out["value"] = None
