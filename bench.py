@@ -83,7 +83,7 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} "
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} "
               "is not supported (the attention path is run on one GPU's "
               "share; see the sharding notes).", file=sys.stderr)
         sys.exit(2)
@@ -91,8 +91,8 @@ def main():
     import torch
 
     import long_context_prefill_swa_amd as lo
-    from workloads import (CONFIGS, affine_inputs, decode_all_steps,
-                           kv_inputs, prefill_inputs)
+    from workloads import (affine_inputs, decode_all_steps, kv_inputs,
+                           prefill_inputs, workload)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -102,10 +102,10 @@ def main():
     run_decode = args.only in (None, "decode")
 
     # ---- prefill_128k inputs ------------------------------------------------
-    pc = CONFIGS[4]
+    pc, pc_id = workload("prefill_128k")
     if run_prefill:
         log(f"[bench] generating {pc.name} inputs")
-        px = prefill_inputs(pc, 4, dev)
+        px = prefill_inputs(pc, pc_id, dev)
         kc4 = torch.empty((pc.B, pc.Hkv, pc.T, pc.D), dtype=torch.bfloat16,
                           device=dev)
         vc4 = torch.empty_like(kc4)
@@ -117,7 +117,7 @@ def main():
             pc.T), dev)
 
     # ---- decode_pair inputs -----------------------------------------------
-    dc = CONFIGS[3]
+    dc, dc_id = workload("decode_pair_b64")
     n_dec = dc.decode_steps
     if run_decode:
         log(f"[bench] generating {dc.name} inputs")
@@ -126,11 +126,11 @@ def main():
                           device=dev)
         vc3 = torch.empty_like(kc3)
         cl3 = torch.zeros(dc.B, dtype=torch.int32, device=dev)
-        k0, v0 = kv_inputs(dc, 3, dev)
+        k0, v0 = kv_inputs(dc, dc_id, dev)
         lo.orthros_kv_append(kc3, vc3, cl3, k0, v0)
         del k0, v0
-        a3, b3, ax3, bx3 = affine_inputs(dc, 3, dev)
-        st = decode_all_steps(dc, 3, device=dev)
+        a3, b3, ax3, bx3 = affine_inputs(dc, dc_id, dev)
+        st = decode_all_steps(dc, dc_id, device=dev)
         o3 = torch.empty((dc.B, dc.Hq, dc.D), dtype=torch.bfloat16, device=dev)
         ox3 = torch.empty_like(o3)
         ws3 = lo.workspace(lo.orthros_workspace_bytes(

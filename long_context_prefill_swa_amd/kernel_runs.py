@@ -33,8 +33,8 @@ def main():
     import torch
 
     import long_context_prefill_swa_amd as lo
-    from workloads import (CONFIGS, affine_inputs, decode_all_steps,
-                           kv_inputs, prefill_inputs)
+    from workloads import (affine_inputs, decode_all_steps, kv_inputs,
+                           prefill_inputs, workload)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -50,8 +50,8 @@ def main():
 
     lo.lib()
     if args.target in ("swa_128k", "global_128k"):
-        pc = CONFIGS[4]
-        px = prefill_inputs(pc, 4, dev)
+        pc, pc_id = workload("prefill_128k")
+        px = prefill_inputs(pc, pc_id, dev)
         kc = torch.empty((pc.B, pc.Hkv, pc.T, pc.D), dtype=torch.bfloat16,
                          device=dev)
         vc = torch.empty_like(kc)
@@ -69,17 +69,17 @@ def main():
             run = lambda: lo.orthros_global_xattn(  # noqa: E731
                 px.qx_pre, px.alpha_x, px.beta_x, kc, vc, ox, pc.T_in, ws=ws)
     else:
-        dc = CONFIGS[3]
+        dc, dc_id = workload("decode_pair_b64")
         cap = dc.T + args.reps
         kc = torch.empty((dc.B, dc.Hkv, cap, dc.D), dtype=torch.bfloat16,
                          device=dev)
         vc = torch.empty_like(kc)
         cl = torch.zeros(dc.B, dtype=torch.int32, device=dev)
-        k0, v0 = kv_inputs(dc, 3, dev)
+        k0, v0 = kv_inputs(dc, dc_id, dev)
         lo.orthros_kv_append(kc, vc, cl, k0, v0)
         del k0, v0
-        a, b, ax, bx = affine_inputs(dc, 3, dev)
-        st = decode_all_steps(dc, 3, steps=args.reps, device=dev)
+        a, b, ax, bx = affine_inputs(dc, dc_id, dev)
+        st = decode_all_steps(dc, dc_id, steps=args.reps, device=dev)
         o = torch.empty((dc.B, dc.Hq, dc.D), dtype=torch.bfloat16, device=dev)
         ox = torch.empty_like(o)
         ws = lo.workspace(lo.orthros_workspace_bytes(

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped where no GPU is visible (they still run under
-    # -m gpu on the GPU machine); CPU tests never touch the device.
+    # -m gpu on a GPU machine); CPU tests never touch the device.
     try:
         import torch
         has_gpu = torch.cuda.is_available()

@@ -15,8 +15,8 @@ import torch
 import long_context_prefill_swa_amd as lo
 import oracle
 from gpu_util import compare, f64, say
-from workloads import (CONFIGS, affine_inputs, decode_all_steps, kv_inputs,
-                       prefill_inputs)
+from workloads import (affine_inputs, decode_all_steps, kv_inputs,
+                       prefill_inputs, workload)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -65,9 +65,9 @@ def prefill(cfg, cfg_id, W=None):
     return x, o, ox
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 4])
-def test_prefill_configuration_sampled(cfg_id):
-    cfg = CONFIGS[cfg_id]
+@pytest.mark.parametrize("name", ["prefill_32k", "sft_dual_8k", "prefill_128k"])
+def test_prefill_configuration_sampled(name):
+    cfg, cfg_id = workload(name)
     say(f"[full size] {cfg.name}")
     x, o, ox = prefill(cfg, cfg_id)
     k_host, v_host = f64(x.k), f64(x.v)
@@ -91,9 +91,9 @@ def test_prefill_configuration_sampled(cfg_id):
 
 def test_long_prefill_full_causal_sampled():
     """The same-T full causal run used for the speedup ratio (W = T)."""
-    cfg = CONFIGS[4]
+    cfg, cfg_id = workload("prefill_128k")
     say("[full size] prefill_128k full causal")
-    x, o, _ = prefill(cfg, 4, W=cfg.T)
+    x, o, _ = prefill(cfg, cfg_id, W=cfg.T)
     k_host, v_host = f64(x.k), f64(x.v)
     ts = [0, 1, 4095, 4096, 65535, cfg.T - 1]
     check_rows(o, x.q_pre, x.alpha, x.beta, k_host, v_host, ts, None,
@@ -101,19 +101,19 @@ def test_long_prefill_full_causal_sampled():
 
 
 def test_decode_pair_configuration_sampled():
-    cfg = CONFIGS[3]
+    cfg, cfg_id = workload("decode_pair_b64")
     B, Hq, Hkv, D, L0, W = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.T, cfg.W
     steps = cfg.decode_steps
     say(f"[full size] {cfg.name}: {steps} steps")
-    k0, v0 = kv_inputs(cfg, 3, DEV)          # the 32768 cached tokens
-    st = decode_all_steps(cfg, 3, device=DEV)
+    k0, v0 = kv_inputs(cfg, cfg_id, DEV)          # the 32768 cached tokens
+    st = decode_all_steps(cfg, cfg_id, device=DEV)
     cap = L0 + steps
     kc = torch.empty((B, Hkv, cap, D), dtype=torch.bfloat16, device=DEV)
     vc = torch.empty_like(kc)
     cl = torch.zeros(B, dtype=torch.int32, device=DEV)
     lo.orthros_kv_append(kc, vc, cl, k0, v0)
     del k0, v0
-    a, b, ax, bx = affine_inputs(cfg, 3, DEV)
+    a, b, ax, bx = affine_inputs(cfg, cfg_id, DEV)
     keep = {0, 1, 127, 255}
     outs = {}
     ws = lo.workspace(lo.orthros_workspace_bytes(lo.ORTHROS_OP_DECODE_PAIR, B,

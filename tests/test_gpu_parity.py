@@ -11,7 +11,7 @@ import torch
 import long_context_prefill_swa_amd as lo
 import oracle
 from gpu_util import TOL, compare, f64, make_cache, say
-from workloads import CONFIGS, normal, prefill_inputs
+from workloads import normal, prefill_inputs, workload
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -45,9 +45,10 @@ def oracle_swa(q, a, b, k, v, W, head_map=None, rows=None):
 
 @pytest.mark.parametrize("W,identity", [(16, False), (64, True)])
 def test_tiny_fp32_configuration(W, identity):
-    cfg = CONFIGS[0].with_(W=W, identity_affine=identity)
+    tiny, tiny_id = workload("tiny_f32")
+    cfg = tiny.with_(W=W, identity_affine=identity)
     say(f"[tiny fp32] W={W} identity={identity}")
-    x = prefill_inputs(cfg, 0, DEV)
+    x = prefill_inputs(cfg, tiny_id, DEV)
     o = run_swa(x.q_pre, x.alpha, x.beta, x.k, x.v, W)
     ref = oracle_swa(x.q_pre, x.alpha, x.beta, x.k, x.v, W)
     compare(o, ref, torch.float32, "swa")

@@ -26,7 +26,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
-from workloads import CONFIGS, prefill_inputs
+from workloads import prefill_inputs, workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -83,8 +83,9 @@ def test_identity_affine_full_window_is_causal_attention(B, T, Hq, Hkv, D, W):
 
 
 def test_tiny_config_identity_run_matches_causal():
-    cfg = CONFIGS[0].with_(W=64, identity_affine=True)
-    x = prefill_inputs(cfg, 0)
+    tiny, tiny_id = workload("tiny_f32")
+    cfg = tiny.with_(W=64, identity_affine=True)
+    x = prefill_inputs(cfg, tiny_id)
     q, k, v = (t.double().numpy() for t in (x.q_pre, x.k, x.v))
     o, _ = oracle.swa(q, x.alpha.numpy(), x.beta.numpy(), k, v, cfg.W)
     np.testing.assert_allclose(o, sdpa(q, k, v, causal=True), atol=1e-12)

@@ -62,6 +62,14 @@ CONFIGS = [
            T_out=1, dtype="bf16", notes="long-context prefill + causal"),
 ]
 
+def workload(name: str):
+    """(config, seed-space id) of the workload called `name`."""
+    for i, c in enumerate(CONFIGS):
+        if c.name == name:
+            return c, i
+    raise KeyError(name)
+
+
 # Tensor ids inside a configuration's seed space.
 _TID = {"q_pre": 1, "qx_pre": 2, "k": 3, "v": 4, "alpha": 5, "beta": 6,
         "alpha_x": 7, "beta_x": 8}
