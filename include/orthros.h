@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 1
+#define ORTHROS_ABI_VERSION 2
 
 /* dtype codes */
 #define ORTHROS_F32 0
@@ -210,10 +210,75 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
                         int dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Paged K/V cache (variable-length batched decoding).
+ *
+ * Pages: paper text §3.3 (decoding is bound by memory I/O; batched decoding
+ * raises the useful work per byte) and §5, Limitation and Future Work
+ * (fitting the decoding mechanism into modern inference frameworks, for
+ * single-sample and batched decoding, is left open; the full cache is
+ * kept). Layout choice, not from the pages: a pool of fixed-size pages
+ * shared by all sequences, so lengths can differ and grow without moving
+ * rows.
+ *
+ *   k_pool, v_pool [dev] [n_pages, Hkv, page_size, D] dtype
+ *   block_table    [dev] int32 [B, max_pages]: key i of batch entry b lives
+ *                  in page block_table[b * max_pages + i / page_size], row
+ *                  i % page_size. Entries must lie in [0, n_pages); pages may
+ *                  be shared only by rows that are never written twice.
+ *   page_size      power of two, 32 <= page_size <= 65536
+ *   cache_len      [dev] int32 [B], per-sequence lengths (ragged)
+ * A block-table entry outside [0, n_pages) never causes an out-of-range
+ * access: the rows it would address are skipped (append) or its page is
+ * replaced by page 0 (decode), the sticky device flag is raised and the
+ * outputs of that batch entry are undefined.
+ */
+
+/*
+ * orthros_kv_append_paged - orthros_kv_append for a paged cache: for every
+ * b, rows cache_len[b] .. cache_len[b]+n_new-1 receive k_new[b, 0..n_new-1]
+ * / v_new[b, ...] ([B, n_new, Hkv, D]); then cache_len[b] += n_new. A batch
+ * entry whose new length exceeds max_pages * page_size is skipped and
+ * raises the device flag (ECAPACITY from orthros_check_device_errors).
+ * Errors: EINVAL, EUNSUPPORTED (dtype, D), EHIP.
+ */
+int orthros_kv_append_paged(void *k_pool, void *v_pool, int64_t n_pages,
+                            int page_size, const int32_t *block_table,
+                            int max_pages, int32_t *cache_len,
+                            const void *k_new, const void *v_new, int B,
+                            int n_new, int Hkv, int D, int dtype,
+                            void *stream);
+
+/*
+ * orthros_decode_pair_paged - orthros_decode_pair on a paged cache, with
+ * per-sequence (ragged) lengths: for each b with old length n = cache_len[b]
+ * the new row is stored at key n, the base query attends keys
+ * [max(0, n-W+1), n], the output query keys [0, n], then cache_len[b] =
+ * n + 1. bf16 with D = 128 only.
+ *
+ *   max_len_after  host upper bound of cache_len[b] + 1 over all b,
+ *                  1 <= max_len_after <= max_pages * page_size
+ *   ws, ws_bytes   scratch of orthros_workspace_bytes(
+ *                  ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after)
+ * Other arguments as orthros_decode_pair.
+ * Errors: EINVAL, EUNSUPPORTED (dtype or D), ECAPACITY, EWORKSPACE, EHIP.
+ */
+int orthros_decode_pair_paged(const void *q_pre, const void *qx_pre,
+                              const float *alpha, const float *beta,
+                              const float *alpha_x, const float *beta_x,
+                              const void *k_new, const void *v_new,
+                              void *k_pool, void *v_pool, int64_t n_pages,
+                              int page_size, const int32_t *block_table,
+                              int max_pages, int32_t *cache_len, void *o,
+                              void *o_x, int B, int Hq, int Hkv, int D,
+                              int64_t max_len_after, int W,
+                              const int32_t *head_map, int dtype, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/*
  * Scratch bytes needed by orthros_global_xattn (op ORTHROS_OP_GLOBAL_XATTN,
  * max_len = T_in + T_out) or orthros_decode_pair (op ORTHROS_OP_DECODE_PAIR,
- * T_out = 1, max_len = max_len_after). Returns 0 for an unknown op or
- * invalid sizes. Pure host function.
+ * T_out = 1, max_len = max_len_after; also orthros_decode_pair_paged).
+ * Returns 0 for an unknown op or invalid sizes. Pure host function.
  */
 size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
                                int T_out, int64_t max_len);

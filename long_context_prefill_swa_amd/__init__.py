@@ -20,7 +20,8 @@ __all__ = [
     "ORTHROS_F32", "ORTHROS_BF16", "ORTHROS_OP_GLOBAL_XATTN",
     "ORTHROS_OP_DECODE_PAIR", "OrthrosError", "lib", "library_path",
     "orthros_kv_append", "orthros_swa_prefill", "orthros_global_xattn",
-    "orthros_decode_pair", "orthros_workspace_bytes",
+    "orthros_decode_pair", "orthros_kv_append_paged",
+    "orthros_decode_pair_paged", "orthros_workspace_bytes",
     "orthros_check_device_errors", "orthros_abi_version",
     "orthros_strerror", "orthros_last_error", "workspace",
 ]
@@ -61,6 +62,12 @@ def lib():
     L.orthros_decode_pair.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, i32, i32, i32, i32, i64,
                                       i64, i32, vp, i32, vp, sz, vp]
+    L.orthros_kv_append_paged.argtypes = [vp, vp, i64, i32, vp, i32, vp, vp,
+                                          vp, i32, i32, i32, i32, i32, vp]
+    L.orthros_decode_pair_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, vp, i64, i32, vp, i32, vp,
+                                            vp, vp, i32, i32, i32, i32, i64,
+                                            i32, vp, i32, vp, sz, vp]
     L.orthros_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i64]
     L.orthros_workspace_bytes.restype = sz
     L.orthros_strerror.argtypes = [i32]
@@ -71,6 +78,7 @@ def lib():
     L.orthros_abi_version.argtypes = []
     for name in ("orthros_kv_append", "orthros_swa_prefill",
                  "orthros_global_xattn", "orthros_decode_pair",
+                 "orthros_kv_append_paged", "orthros_decode_pair_paged",
                  "orthros_check_device_errors", "orthros_abi_version"):
         getattr(L, name).restype = i32
     _lib = L
@@ -222,6 +230,70 @@ def orthros_decode_pair(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
         _dev(cache_len, "cache_len", torch.int32), _dev(o, "o", dt),
         _dev(o_x, "o_x", dt), B, Hq, Hkv, D, cap, int(max_len_after), int(W),
         hm, _dtype_code(q_pre), _dev(ws, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream, q_pre)))
+
+
+def _paged(k_pool, v_pool, block_table):
+    n_pages, Hkv, page_size, D = k_pool.shape
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool shapes differ")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_pages]")
+    return n_pages, Hkv, page_size, D, block_table.shape[1]
+
+
+def orthros_kv_append_paged(k_pool, v_pool, block_table, cache_len, k_new,
+                            v_new, stream=None):
+    """Paged cache append. k_pool, v_pool [n_pages, Hkv, page_size, D];
+    block_table int32 [B, max_pages]; k_new, v_new [B, n, Hkv, D]."""
+    n_pages, Hkv, page_size, D, max_pages = _paged(k_pool, v_pool, block_table)
+    B, n_new = k_new.shape[0], k_new.shape[1]
+    if tuple(k_new.shape) != (B, n_new, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, n, Hkv, D]")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B rows")
+    dt = k_pool.dtype
+    _check(lib().orthros_kv_append_paged(
+        _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt), n_pages,
+        page_size, _dev(block_table, "block_table", torch.int32), max_pages,
+        _dev(cache_len, "cache_len", torch.int32), _dev(k_new, "k_new", dt),
+        _dev(v_new, "v_new", dt), B, n_new, Hkv, D, _dtype_code(k_pool),
+        _stream(stream, k_pool)))
+
+
+def orthros_decode_pair_paged(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
+                              k_new, v_new, k_pool, v_pool, block_table,
+                              cache_len, o, o_x, max_len_after, W,
+                              head_map=None, ws=None, stream=None):
+    """Decode pair step on a paged cache (see orthros_kv_append_paged)."""
+    n_pages, Hkv, page_size, D, max_pages = _paged(k_pool, v_pool, block_table)
+    B, Hq = q_pre.shape[0], q_pre.shape[1]
+    if tuple(q_pre.shape) != (B, Hq, D):
+        raise ValueError("q_pre must be [B, Hq, D]")
+    if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, Hkv, D]")
+    if qx_pre.shape != q_pre.shape or o.shape != q_pre.shape or o_x.shape != q_pre.shape:
+        raise ValueError("q_pre, qx_pre, o, o_x must all be [B, Hq, D]")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have B rows")
+    dt = q_pre.dtype
+    if ws is None:
+        need = orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D,
+                                       1, int(max_len_after))
+        ws = workspace(need, q_pre.device) if need else None
+    hm, _keep = _map(head_map)
+    f32 = torch.float32
+    _check(lib().orthros_decode_pair_paged(
+        _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt),
+        _dev(alpha, "alpha", f32), _dev(beta, "beta", f32),
+        _dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32),
+        _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
+        _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt), n_pages,
+        page_size, _dev(block_table, "block_table", torch.int32), max_pages,
+        _dev(cache_len, "cache_len", torch.int32), _dev(o, "o", dt),
+        _dev(o_x, "o_x", dt), B, Hq, Hkv, D, int(max_len_after), int(W), hm,
+        _dtype_code(q_pre), _dev(ws, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream, q_pre)))
 

@@ -72,6 +72,18 @@ hipError_t launch_rowwise(const void *q, const float *alpha, const float *beta,
                           int W, const int32_t *cache_len, const HeadMap &map,
                           int is_bf16, hipStream_t stream);
 
+// Paged variant: row len+i of batch entry b goes to page
+// block_table[b * max_pages + (len + i) >> page_log2]; entries outside
+// [0, n_pages) or lengths beyond max_pages pages skip the batch entry and
+// raise *flag. Then the lengths are advanced.
+hipError_t launch_kv_append_paged(void *k_pool, void *v_pool,
+                                  int32_t *cache_len, const void *k_new,
+                                  const void *v_new, int B, int n_new,
+                                  int Hkv, int row_bytes, int64_t n_pages,
+                                  int page_log2, const int32_t *block_table,
+                                  int max_pages, int *flag,
+                                  hipStream_t stream);
+
 // Increments cache_len[b] by n where the result stays within [0, cap].
 hipError_t launch_len_bump(int32_t *cache_len, int B, int n, int64_t cap,
                            hipStream_t stream);
@@ -107,6 +119,14 @@ struct SplitKVArgs {
   int64_t ws_acc_offset;     // float offset of the unnormalised outputs
   int32_t *ws_len;           // decode: per-batch old length or -1
   int *flag;
+  // Paged cache (block_table != nullptr): k_cache / v_cache are pools of
+  // n_pages pages [n_pages, n_kv_heads, page_size, D]; key i of batch entry
+  // b sits in page block_table[b * max_pages + i / page_size], row
+  // i % page_size. page_size is a power of two >= 32.
+  const int32_t *block_table;
+  int max_pages;
+  int page_log2;
+  int64_t n_pages;
 };
 int splitkv_rows(int n_streams, int n_pos, int gsize);
 size_t splitkv_ws_bytes(int B, int n_groups, int rows, int n_chunks, int D);

@@ -429,6 +429,147 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
   return ORTHROS_OK;
 }
 
+// Shared checks of the paged-cache arguments; on success *log2 = log2 of
+// page_size.
+static int check_paged(void *k_pool, void *v_pool, int64_t n_pages,
+                       int page_size, const int32_t *block_table,
+                       int max_pages, int Hkv, int D, int dtype, int *log2) {
+  if (page_size < 32 || page_size > 65536 || (page_size & (page_size - 1)))
+    return fail(ORTHROS_EINVAL,
+                "page_size=%d must be a power of two in [32, 65536]", page_size);
+  if (n_pages < 1 || n_pages > INT32_MAX)
+    return fail(ORTHROS_EINVAL, "n_pages=%lld outside [1, 2^31-1]",
+                (long long)n_pages);
+  if (max_pages < 1)
+    return fail(ORTHROS_EINVAL, "max_pages=%d must be >= 1", max_pages);
+  if (!k_pool || !v_pool || !block_table)
+    return fail(ORTHROS_EINVAL, "null pointer argument");
+  int64_t n_elems;
+  if (!tensor_elems(&n_elems, {n_pages, Hkv, page_size, D, (int64_t)esize(dtype)}))
+    return fail(ORTHROS_EINVAL, "page pool size overflows");
+  if ((int64_t)max_pages * page_size > INT32_MAX)
+    return fail(ORTHROS_EINVAL, "max_pages * page_size exceeds 2^31-1");
+  int l = 0;
+  while ((1 << l) < page_size) ++l;
+  *log2 = l;
+  return ORTHROS_OK;
+}
+
+int orthros_kv_append_paged(void *k_pool, void *v_pool, int64_t n_pages,
+                            int page_size, const int32_t *block_table,
+                            int max_pages, int32_t *cache_len,
+                            const void *k_new, const void *v_new, int B,
+                            int n_new, int Hkv, int D, int dtype,
+                            void *stream) {
+  clear_error();
+  int rc = check_dtype_d(dtype, D);
+  if (rc) return rc;
+  if (B < 0 || n_new < 0) return fail(ORTHROS_EINVAL, "negative size (B=%d, n_new=%d)", B, n_new);
+  if (Hkv < 1 || Hkv > ORTHROS_MAX_HEADS) return fail(ORTHROS_EINVAL, "Hkv=%d outside [1, %d]", Hkv, ORTHROS_MAX_HEADS);
+  int log2 = 0;
+  if ((rc = check_paged(k_pool, v_pool, n_pages, page_size, block_table,
+                        max_pages, Hkv, D, dtype, &log2)))
+    return rc;
+  if ((int64_t)n_new > (int64_t)max_pages * page_size)
+    return fail(ORTHROS_ECAPACITY, "n_new=%d exceeds max_pages * page_size", n_new);
+  if (B == 0 || n_new == 0) return ORTHROS_OK;
+  if (!cache_len || !k_new || !v_new) return fail(ORTHROS_EINVAL, "null pointer argument");
+  int *flag = nullptr;
+  hipError_t e = device_flag_ptr(&flag);
+  if (e != hipSuccess) return hip_fail("device flag", e);
+  e = launch_kv_append_paged(k_pool, v_pool, cache_len, k_new, v_new, B,
+                             n_new, Hkv, D * (int)esize(dtype), n_pages, log2,
+                             block_table, max_pages, flag, as_stream(stream));
+  if (e != hipSuccess) return hip_fail("kv_append_paged launch", e);
+  return ORTHROS_OK;
+}
+
+int orthros_decode_pair_paged(const void *q_pre, const void *qx_pre,
+                              const float *alpha, const float *beta,
+                              const float *alpha_x, const float *beta_x,
+                              const void *k_new, const void *v_new,
+                              void *k_pool, void *v_pool, int64_t n_pages,
+                              int page_size, const int32_t *block_table,
+                              int max_pages, int32_t *cache_len, void *o,
+                              void *o_x, int B, int Hq, int Hkv, int D,
+                              int64_t max_len_after, int W,
+                              const int32_t *head_map, int dtype, void *ws,
+                              size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_dtype_d(dtype, D);
+  if (rc) return rc;
+  if (dtype != ORTHROS_BF16 || D != 128)
+    return fail(ORTHROS_EUNSUPPORTED,
+                "the paged decode pair supports bf16 with D=128 (got dtype %d, D=%d)",
+                dtype, D);
+  if ((rc = check_heads(Hq, Hkv))) return rc;
+  if (B < 0) return fail(ORTHROS_EINVAL, "negative batch B=%d", B);
+  if (W < 1) return fail(ORTHROS_EINVAL, "window W=%d must be >= 1", W);
+  int log2 = 0;
+  if ((rc = check_paged(k_pool, v_pool, n_pages, page_size, block_table,
+                        max_pages, Hkv, D, dtype, &log2)))
+    return rc;
+  if (max_len_after < 1)
+    return fail(ORTHROS_EINVAL, "max_len_after=%lld must be >= 1", (long long)max_len_after);
+  const int64_t cap = (int64_t)max_pages * page_size;
+  if (max_len_after > cap)
+    return fail(ORTHROS_ECAPACITY, "max_len_after=%lld exceeds max_pages * page_size = %lld",
+                (long long)max_len_after, (long long)cap);
+  HeadMap map;
+  HeadGroups groups;
+  if ((rc = build_maps(head_map, Hq, Hkv, &map, &groups))) return rc;
+  if (B == 0) return ORTHROS_OK;
+  if (!q_pre || !qx_pre || !alpha || !beta || !alpha_x || !beta_x || !k_new ||
+      !v_new || !cache_len || !o || !o_x)
+    return fail(ORTHROS_EINVAL, "null pointer argument");
+  if (!mfma_eligible(dtype, D, max_len_after,
+                     {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
+                      v_new, k_pool, v_pool, o, o_x}))
+    return fail(ORTHROS_EINVAL, "tensors must be 16-byte aligned");
+  const SplitPlan plan = plan_split(B, 2, 1, groups, D, max_len_after);
+  if (!plan.use)
+    return fail(ORTHROS_EUNSUPPORTED, "no split plan for these sizes");
+  if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))
+    return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
+                plan.ws_bytes, ws ? ws_bytes : (size_t)0);
+  int *flag = nullptr;
+  hipError_t e = device_flag_ptr(&flag);
+  if (e != hipSuccess) return hip_fail("device flag", e);
+  SplitKVArgs a = {};
+  a.q[0] = q_pre;
+  a.q[1] = qx_pre;
+  a.alpha[0] = alpha;
+  a.alpha[1] = alpha_x;
+  a.beta[0] = beta;
+  a.beta[1] = beta_x;
+  a.o[0] = o;
+  a.o[1] = o_x;
+  a.W[0] = W;
+  a.W[1] = 0;
+  a.n_streams = 2;
+  a.n_pos = 1;
+  a.B = B;
+  a.Hq = Hq;
+  a.n_kv_heads = Hkv;
+  a.cap = cap;
+  a.pos0 = 0;
+  a.cache_len = cache_len;
+  a.k_cache = k_pool;
+  a.v_cache = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.max_len = max_len_after;
+  a.flag = flag;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.page_log2 = log2;
+  a.n_pages = n_pages;
+  fill_ws(&a, ws, plan, B, groups.n_groups);
+  e = launch_splitkv(a, groups, as_stream(stream));
+  if (e != hipSuccess) return hip_fail("decode_pair_paged launch", e);
+  return ORTHROS_OK;
+}
+
 int orthros_check_device_errors(void *stream) {
   clear_error();
   hipError_t e = hipStreamSynchronize(as_stream(stream));

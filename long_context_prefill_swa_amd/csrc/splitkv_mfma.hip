@@ -97,12 +97,14 @@ struct Slice {
   uint4 v[8];
 };
 
+template <bool Paged>
 __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
     SplitKVArgs a, HeadGroups groups) {
   __shared__ __attribute__((aligned(16))) SplitSmem sm;
 
   const int c = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 15, g4 = lane >> 4;
   const int gsize = groups.gsize;
   const int rows = a.n_streams * a.n_pos * gsize;
@@ -141,20 +143,55 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
     r_hi = min(t, k_stop - 1);
   }
 
-  // cache slab of this (batch, KV head); rows [0, k_stop) are readable
-  // through buffer resources, reads past them return zeros
+  // Contiguous cache: the slab of this (batch, KV head), rows [0, k_stop)
+  // readable through buffer resources (reads past them return zeros).
+  // Paged cache: each 32-key slice lies in one page (page_size >= 32); lane
+  // l holds the block-table entry of the chunk's l-th page (a chunk spans at
+  // most 64 pages), out-of-range entries are clamped and raise the flag.
   const int64_t head_off = ((int64_t)b * a.n_kv_heads + kvh) * a.cap * D;
   uint16_t *kc = (uint16_t *)a.k_cache + head_off;
   uint16_t *vc = (uint16_t *)a.v_cache + head_off;
+  int my_page = 0, my_ok = 1;
+  int64_t first_page = 0;
+  int64_t page_elems = 0;  // elements of one KV head's part of a page
+  if constexpr (Paged) {
+    page_elems = (int64_t)D << a.page_log2;
+    first_page = k_begin >> a.page_log2;
+    const int64_t pi = first_page + lane;
+    if (pi * (1 << a.page_log2) < k_stop && pi < a.max_pages) {
+      const int32_t e = a.block_table[(int64_t)b * a.max_pages + pi];
+      const bool ok = e >= 0 && e < a.n_pages;
+      if (!ok) atomicOr(a.flag, 1);
+      my_page = ok ? e : 0;
+      my_ok = ok;
+    }
+  }
+  // Base of key `key`'s page (paged) or of the slab, for this KV head.
+  auto page_slot = [&](int64_t key) {
+    return max(min((int)((key >> a.page_log2) - first_page), 63), 0);
+  };
+  auto page_base = [&](uint16_t *pool, int64_t key) -> uint16_t * {
+    const int page = __builtin_amdgcn_readlane(my_page, page_slot(key));
+    return pool + ((int64_t)page * a.n_kv_heads + kvh) * page_elems;
+  };
   if (a.cache_len && n_old >= k_begin && n_old < k_stop) {
     // Decode: this workgroup's chunk holds the new row. Store it first; it
     // is the only workgroup that reads that row.
-    if (w == 0 && lane < 32) {
+    uint16_t *kd = kc + n_old * D, *vd = vc + n_old * D;
+    if constexpr (Paged) {
+      const int64_t row = n_old & ((1 << a.page_log2) - 1);
+      kd = page_base((uint16_t *)a.k_cache, n_old) + row * D;
+      vd = page_base((uint16_t *)a.v_cache, n_old) + row * D;
+    }
+    bool store = true;
+    if constexpr (Paged)  // an invalid page is not written (flag raised)
+      store = __builtin_amdgcn_readlane(my_ok, page_slot(n_old)) != 0;
+    if (store && w == 0 && lane < 32) {
       const int part = lane & 15;
       const int64_t src_off = ((int64_t)b * a.n_kv_heads + kvh) * D;
       const uint4 *src = (const uint4 *)((const uint16_t *)((lane < 16) ? a.k_new : a.v_new) +
                                          src_off) + part;
-      uint4 *dst = (uint4 *)(((lane < 16) ? kc : vc) + n_old * D) + part;
+      uint4 *dst = (uint4 *)((lane < 16) ? kd : vd) + part;
       *dst = *src;
     }
     __threadfence();
@@ -205,23 +242,37 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
 
   // ---- slice loads ---------------------------------------------------------
   // Slice `it` of this wave covers keys k_begin + 128 it + 32 w + [0, 32).
-  const uint32_t wave_off = (uint32_t)(kSlice * w) * (D * 2);
   const uint32_t k_lane = (uint32_t)col * (D * 2) + 16u * g4;
   const uint32_t v_lane = (uint32_t)g4 * (D * 2) + 16u * col;
   auto load = [&](Slice &sl, int it) {
-    const uint32_t base = (uint32_t)(k_begin + (int64_t)it * kStepKeys) * (D * 2) + wave_off;
+    const int64_t key0 = k_begin + (int64_t)it * kStepKeys + kSlice * w;
+    uint32_t base;
+    __amdgpu_buffer_rsrc_t sk = rk, sv = rv;
+    if constexpr (Paged) {
+      // Resources over this slice's page, ending at the last valid key.
+      const int64_t pkey0 = key0 & ~(int64_t)((1 << a.page_log2) - 1);
+      const int64_t valid = min((int64_t)1 << a.page_log2, k_stop - pkey0);
+      const uint32_t nbytes = valid > 0 ? (uint32_t)valid * (D * 2) : 0u;
+      sk = __builtin_amdgcn_make_buffer_rsrc(
+          page_base((uint16_t *)a.k_cache, key0), 0, nbytes, kBufferWord3);
+      sv = __builtin_amdgcn_make_buffer_rsrc(
+          page_base((uint16_t *)a.v_cache, key0), 0, nbytes, kBufferWord3);
+      base = (uint32_t)(key0 - pkey0) * (D * 2);
+    } else {
+      base = (uint32_t)key0 * (D * 2);
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4)
         sl.k[kt][c4] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rk, base + k_lane + 16u * (D * 2) * kt + 64u * c4, 0, 0));
+                       sk, base + k_lane + 16u * (D * 2) * kt + 64u * c4, 0, 0));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       sl.v[i] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                     rv, base + v_lane + 4u * (D * 2) * i, 0, 0));
+                     sv, base + v_lane + 4u * (D * 2) * i, 0, 0));
   };
 
   // V^T transposed-read addresses: group g4 reads keys 4 g4.. (+16) and
@@ -452,7 +503,8 @@ int splitkv_rows(int n_streams, int n_pos, int gsize) {
 
 // Keys per workgroup: a power of two from 256 to 2048, the largest that still
 // gives every compute unit its two resident workgroups (gfx950 parts have 256
-// compute units). Long caches then run in whole rounds of long-lived
+// compute units). At most 2048, so a chunk of a paged cache spans at most 64
+// pages (one block-table entry per lane). Long caches then run in whole rounds of long-lived
 // workgroups; short ones still spread over the whole chip. Depends on the
 // sizes only, so the workspace query needs no device.
 int splitkv_pick_chunk(int B, int n_groups, int64_t max_len) {
@@ -460,8 +512,7 @@ int splitkv_pick_chunk(int B, int n_groups, int64_t max_len) {
   static const int max_chunk = [] {
     const char *e = getenv("ORTHROS_SPLIT_CHUNK");
     const int v = e ? atoi(e) : 0;
-    return (v == 256 || v == 512 || v == 1024 || v == 2048 || v == 4096) ? v
-                                                                         : 2048;
+    return (v == 256 || v == 512 || v == 1024 || v == 2048) ? v : 2048;
   }();
   int chunk = max_chunk;
   while (chunk > 256 &&
@@ -485,8 +536,12 @@ hipError_t launch_splitkv(const SplitKVArgs &a_in, const HeadGroups &groups,
   SplitKVArgs a = a_in;
   const int rows = splitkv_rows(a.n_streams, a.n_pos, groups.gsize);
   dim3 grid(a.n_chunks, groups.n_groups, a.B);
-  hipLaunchKernelGGL(splitkv_kernel, grid, dim3(kThreads), 0, stream, a,
-                     groups);
+  if (a.block_table)
+    hipLaunchKernelGGL(splitkv_kernel<true>, grid, dim3(kThreads), 0, stream,
+                       a, groups);
+  else
+    hipLaunchKernelGGL(splitkv_kernel<false>, grid, dim3(kThreads), 0, stream,
+                       a, groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(splitkv_merge_kernel, dim3(rows, groups.n_groups, a.B),

@@ -32,10 +32,11 @@ def declared_functions():
                                  r"(orthros_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("orthros_kv_append", "orthros_swa_prefill",
-              "orthros_global_xattn", "orthros_decode_pair"):
+              "orthros_global_xattn", "orthros_decode_pair",
+              "orthros_kv_append_paged", "orthros_decode_pair_paged"):
         assert n in names
 
 
@@ -50,7 +51,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.orthros_abi_version() == 1
+    assert L.orthros_abi_version() == 2
     for code in (OK, EINVAL, EUNSUP, ECAP, EWS, EHIP):
         assert L.orthros_strerror(code)
     assert b"unknown" in L.orthros_strerror(42)
@@ -166,3 +167,71 @@ def test_workspace_bytes(L):
     assert ws(1, 4, 32, 8, 128, 2048, 8192) == 0
     # non-128 head dimensions run the generic kernel without workspace
     assert ws(1, 1, 2, 2, 16, 1, 64) == 0
+
+
+def paged_append(L, **kw):
+    a = dict(n_pages=16, page_size=64, max_pages=4, B=2, n=10, Hkv=2, D=128,
+             dtype=BF16, bt=FAKE, cl=FAKE)
+    a.update(kw)
+    return L.orthros_kv_append_paged(FAKE, FAKE, a["n_pages"], a["page_size"],
+                                     a["bt"], a["max_pages"], a["cl"], FAKE,
+                                     FAKE, a["B"], a["n"], a["Hkv"], a["D"],
+                                     a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(page_size=48), EINVAL, "power of two"),
+    (dict(page_size=16), EINVAL, "power of two"),
+    (dict(page_size=1 << 17), EINVAL, "power of two"),
+    (dict(n_pages=0), EINVAL, "n_pages"),
+    (dict(max_pages=0), EINVAL, "max_pages"),
+    (dict(bt=None), EINVAL, "null"),
+    (dict(cl=None), EINVAL, "null"),
+    (dict(n=257), ECAP, "max_pages"),
+    (dict(dtype=5), EUNSUP, "dtype"),
+    (dict(B=-1), EINVAL, "negative"),
+])
+def test_kv_append_paged_rejects(L, kw, code, needle):
+    assert paged_append(L, **kw) == code
+    assert needle in last(L)
+
+
+def test_kv_append_paged_zero_sized(L):
+    assert paged_append(L, B=0) == OK
+    assert paged_append(L, n=0) == OK
+
+
+def paged_decode(L, **kw):
+    a = dict(n_pages=16, page_size=64, max_pages=4, B=2, Hq=4, Hkv=2, D=128,
+             max_len=200, W=16, dtype=BF16, ws=None, ws_bytes=0, bt=FAKE,
+             cl=FAKE)
+    a.update(kw)
+    return L.orthros_decode_pair_paged(
+        *([FAKE] * 10), a["n_pages"], a["page_size"], a["bt"],
+        a["max_pages"], a["cl"], FAKE, FAKE, a["B"], a["Hq"], a["Hkv"],
+        a["D"], a["max_len"], a["W"], None, a["dtype"], a["ws"],
+        a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=F32), EUNSUP, "bf16"),
+    (dict(D=64), EUNSUP, "bf16"),
+    (dict(page_size=100), EINVAL, "power of two"),
+    (dict(max_len=257), ECAP, "max_pages"),
+    (dict(max_len=0), EINVAL, "max_len_after"),
+    (dict(W=0), EINVAL, "window"),
+    (dict(bt=None), EINVAL, "null"),
+    (dict(cl=None), EINVAL, "null"),
+    (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
+    (dict(), EWS, "workspace"),
+])
+def test_decode_pair_paged_rejects(L, kw, code, needle):
+    assert paged_decode(L, **kw) == code
+    assert needle in last(L)
+
+
+def test_decode_pair_paged_workspace_matches_contiguous(L):
+    need = L.orthros_workspace_bytes(2, 2, 4, 2, 128, 1, 200)
+    assert need > 0
+    assert paged_decode(L, ws=FAKE, ws_bytes=need - 16) == EWS
+    assert paged_decode(L, B=0) == OK
