@@ -97,6 +97,17 @@ hipError_t launch_band_mfma(const void *q, const float *alpha,
                             const HeadGroups &groups, int n_kv,
                             hipStream_t stream);
 
+// Rolling-window attention for small windows, bf16, D = 128, 4 query heads
+// per KV head, rows at positions 0 .. nrows-1: key tiles per query tile
+// band_roll_tiles(W) must be 3 (65 < W <= 129).
+int band_roll_tiles(int W);
+hipError_t launch_band_roll(const void *q, const float *alpha,
+                            const float *beta, const void *k_cache,
+                            const void *v_cache, void *o, int B, int nrows,
+                            int Hq, int64_t cap, int W,
+                            const HeadGroups &groups, int n_kv,
+                            hipStream_t stream);
+
 // Split-KV flash decode, bf16, D = 128, MFMA. See splitkv_mfma.hip.
 struct SplitKVArgs {
   const void *q[2];          // [B, n_pos, Hq, D] per stream

@@ -258,7 +258,13 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
       !tensor_elems(&n_elems, {B, T, Hq, D, 2}))
     return fail(ORTHROS_EINVAL, "tensor size overflows");
   hipError_t e;
-  if (mfma_eligible(dtype, D, T, {q_pre, alpha, beta, k_cache, v_cache, o})) {
+  if (mfma_eligible(dtype, D, T, {q_pre, alpha, beta, k_cache, v_cache, o}) &&
+      groups.gsize == 4 && band_roll_tiles(W) == 3) {
+    // small window: the pass streams Q/O through HBM (rolling kernel)
+    e = launch_band_roll(q_pre, alpha, beta, k_cache, v_cache, o, B, T, Hq,
+                         cap, W, groups, Hkv, as_stream(stream));
+  } else if (mfma_eligible(dtype, D, T,
+                           {q_pre, alpha, beta, k_cache, v_cache, o})) {
     e = launch_band_mfma(q_pre, alpha, beta, k_cache, v_cache, o, B, T, Hq,
                          cap, 0, W, groups, Hkv, as_stream(stream));
   } else {

@@ -148,3 +148,15 @@ def test_decode_pair_configuration_sampled():
         # appended rows are the step tokens, bit for bit
         assert torch.equal(kc[bi, :, L0:].permute(1, 0, 2).float(),
                            st.k_new[:, bi].float())
+
+
+def test_long_prefill_trained_window_sampled():
+    """The 128K prefill at the window the paper trains with (W = 128), which
+    runs the rolling-window kernel."""
+    cfg, cfg_id = workload("prefill_128k")
+    say("[full size] prefill_128k W=128")
+    x, o, _ = prefill(cfg, cfg_id, W=128)
+    k_host, v_host = f64(x.k), f64(x.v)
+    ts = sample_rows(cfg.T, 128, 24, cfg_id + 7)
+    check_rows(o, x.q_pre, x.alpha, x.beta, k_host, v_host, ts, 128,
+               "base stream W=128")

@@ -116,6 +116,59 @@ def test_swa_bf16_parity(B, T, Hq, Hkv, W):
     compare(o, oracle_swa(q, a, b, k, v, W), dt, "swa")
 
 
+# --- base stream: rolling-window kernel (4 query heads per KV head, three
+# key tiles per query tile: 65 < W <= 129) ------------------------------------
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,W", [
+    (2, 1000, 8, 2, 128),   # the trained window, ragged tail
+    (3, 777, 8, 2, 66),     # smallest three-tile window
+    (1, 576, 8, 2, 129),    # largest; T a multiple of the tile
+    (1, 513, 32, 8, 100),   # eight groups, one row past a tile
+    (2, 63, 8, 2, 128),     # a single partial tile
+])
+def test_swa_rolling_parity(B, T, Hq, Hkv, W):
+    D = 128
+    say(f"[swa rolling] B={B} T={T} Hq={Hq} Hkv={Hkv} W={W}")
+    dt = torch.bfloat16
+    q, k, v = rand((B, T, Hq, D), 14, dt), rand((B, T, Hkv, D), 15, dt), rand((B, T, Hkv, D), 16, dt)
+    a, b = affine_pair(Hq * D, 17)
+    o = run_swa(q, a, b, k, v, W)
+    compare(o, oracle_swa(q, a, b, k, v, W), dt, "swa")
+
+
+def test_swa_rolling_long_segments_sampled():
+    """One group, so each workgroup walks several query tiles through the
+    ring; rows at every segment and tile boundary plus random ones."""
+    B, T, Hq, Hkv, D, W = 1, 40000, 4, 1, 128, 128
+    say(f"[swa rolling long] T={T} W={W}")
+    dt = torch.bfloat16
+    q, k, v = rand((B, T, Hq, D), 18, dt), rand((B, T, Hkv, D), 19, dt), rand((B, T, Hkv, D), 20, dt)
+    a, b = affine_pair(Hq * D, 21)
+    o = run_swa(q, a, b, k, v, W)
+    ts = set()
+    for e in range(0, T, 64):
+        ts.update((e - 1, e, e + 1))
+    ts.update(int(x) for x in np.random.default_rng(22).integers(0, T, 500))
+    ts = sorted(t for t in ts if 0 <= t < T)
+    rows = np.array([(0, t) for t in ts], np.int64)
+    ref = oracle_swa(q, a, b, k, v, W, rows=rows)
+    compare(o[0, ts], ref, dt, f"swa ({len(ts)} rows)")
+
+
+def test_swa_rolling_padded_group():
+    """A head map whose groups hold 3 and 2 query heads (padded to 4)."""
+    hmap = [0, 1, 0, 1, 0]
+    B, T, D, Hkv, W = 2, 300, 128, 2, 128
+    Hq = len(hmap)
+    say(f"[swa rolling head map] {hmap}")
+    dt = torch.bfloat16
+    q, k, v = rand((B, T, Hq, D), 24, dt), rand((B, T, Hkv, D), 25, dt), rand((B, T, Hkv, D), 26, dt)
+    a, b = affine_pair(Hq * D, 27)
+    o = run_swa(q, a, b, k, v, W, head_map=hmap)
+    compare(o, oracle_swa(q, a, b, k, v, W, head_map=np.array(hmap, np.int32)),
+            dt, "swa")
+
+
 @pytest.mark.parametrize("hmap", [[2, 0, 1, 1, 0, 2], [0, 0, 0, 1, 2, 2]])
 def test_swa_custom_head_map(hmap):
     B, T, D, Hkv = 2, 200, 128, 3
