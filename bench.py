@@ -277,6 +277,29 @@ def main():
                          "speedup_vs_swa": t_c / out["prefill"]["ms_swa"]}
         log(f"[bench] causal {t_c:.2f} ms, speedup {t_c / out['prefill']['ms_swa']:.1f}x")
 
+    # ---- the window the paper trains with (W = 128) at the same T ----------
+    if run_prefill:
+        reps, W_s = 3, 128
+        lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4, W_s)
+        torch.cuda.synchronize()
+        e0 = ev()
+        for _ in range(reps):
+            lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4,
+                                   W_s)
+        e1 = ev()
+        torch.cuda.synchronize()
+        t_s = e0.elapsed_time(e1) / reps
+        # every byte of Q, O, K and V crosses HBM once
+        by = 2 * 2 * pc.B * pc.T * pc.D * (pc.Hq + pc.Hkv)
+        out["swa_w128"] = {
+            "ms": t_s, "tokens_per_s": pc.B * pc.T / (t_s * 1e-3),
+            "tflops": 4.0 * pc.D * band_pairs(pc.T, W_s) * pc.Hq * pc.B
+            / (t_s * 1e-3) / 1e12,
+            "algorithmic_bytes": by, "gbps": by / (t_s * 1e-3) / 1e9,
+            "hbm_frac": by / (t_s * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        log(f"[bench] swa W=128: {t_s:.3f} ms, "
+            f"{out['swa_w128']['gbps']:.0f} GB/s")
+
     # ---- paged cache, ragged lengths (variable-length batched decoding) -----
     if run_decode and not args.no_paged:
         del kc3, vc3

@@ -9,19 +9,19 @@
 //
 // Structure (one resident workgroup per compute unit, 8 waves, the 4 query
 // heads of one KV head): a workgroup walks a contiguous segment of 64-row
-// query tiles of one (batch, KV head). Query tile qt attends key tiles
-// qt-NTB+1 .. qt (NTB = ceil((W-1)/64) + 1 = 3 for 65 < W <= 129; other
-// windows run the banded kernel). Those tiles stay in an
-// LDS ring of NTB+1 slots, so each query tile loads ONE new K/V tile (and
-// its queries), which arrive in registers while the current tile is being
-// computed; every byte of Q, K, V and O crosses HBM once.
+// query tiles of one (batch, KV head). Query tile qt needs key tiles qt-2 ..
+// qt at most (W <= 129); those stay in an LDS ring of four slots, so each
+// query tile loads ONE new K/V tile (and its queries), which arrive in
+// registers while the current tile is being computed; every byte of Q, K, V
+// and O crosses HBM once.
 //  * wave w owns 32 rows of query head w % 4 (row block w / 4); the MFMA
 //    layouts are those of the banded kernel: S^T = K Q^T and O^T += V^T P^T
 //    on v_mfma_f32_32x32x16_bf16, the V^T operand read with
 //    ds_read_b64_tr_b16, each lane holding one query row;
-//  * the softmax runs online over the NTB tiles (base 2, lazy rescaling of
-//    the reference maximum, -m seeding the score accumulators), with band
-//    masks only on tiles not inside every row's band;
+//  * the 32 rows of a wave need the keys of NSB = ceil((W-1)/32) + 1
+//    sub-blocks of 32 keys; all their scores are formed first (independent
+//    MFMA chains), so the softmax takes one exact row maximum and needs no
+//    rescaling; band masks only on sub-blocks not inside every row's band;
 //  * alpha (.) q + beta uses alpha, beta pre-scaled by log2(e)/sqrt(D) and
 //    kept in LDS for the workgroup's heads.
 #include "common.h"
@@ -42,28 +42,30 @@ constexpr float kTau = 8.0f;
 constexpr int kBufferWord3 = 0x00020000;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
 }
 
-template <int NTB>
+constexpr int kSlots = 4;  // ring of key tiles: the band's three + the next
+
 struct RollSmem {
-  uint16_t k[NTB + 1][kBN][kKS];
-  uint16_t v[NTB + 1][kBN][kVS];
+  uint16_t k[kSlots][kBN][kKS];
+  uint16_t v[kSlots][kBN][kVS];
   float ab[kGsize][2][D];  // alpha, beta of the group's heads, pre-scaled
 };
 
-template <int NTB>
+template <int NSB>
 __global__ __launch_bounds__(kNT, 2) void band_roll_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ alpha,
     const float *__restrict__ beta, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, uint16_t *__restrict__ o,
     int nrows, int Hq, int n_kv, int64_t cap, int W, int n_qtiles,
     int seg_len, int n_segs, HeadGroups groups) {
-  constexpr int kSlots = NTB + 1;
-  __shared__ __attribute__((aligned(16))) RollSmem<NTB> sm;
+  static_assert(NSB >= 1 && NSB <= 5, "the ring holds three key tiles");
+  __shared__ __attribute__((aligned(16))) RollSmem sm;
 
   const int seg = blockIdx.x % n_segs;
   const int rest = blockIdx.x / n_segs;
@@ -73,7 +75,8 @@ __global__ __launch_bounds__(kNT, 2) void band_roll_kernel(
   const int qt_end = min(qt_begin + seg_len, n_qtiles);
   if (qt_begin >= qt_end) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = tid >> 6;
   const int j = lane & 31, hh = lane >> 5;
   const int kvh = groups.kv[gi];
   const int head = groups.q[gi][w % kGsize];
@@ -117,18 +120,33 @@ __global__ __launch_bounds__(kNT, 2) void band_roll_kernel(
     }
   };
 
-  // raw query rows of a tile for this lane (row 64 qt + 32 ps + j, channels
-  // 16 c + 8 hh .. + 7); rows past the end re-read the last row
+  // Q and O rows of a query tile through a buffer resource based at the
+  // tile's first row of this head: rows past nrows read as zeros and their
+  // stores are dropped. This lane's row 32 ps + j of the tile, channels
+  // 16 c + 8 hh .. + 7 (loads) / 32 dt + 8 q4 + 4 hh .. + 3 (stores).
+  const uint32_t row_bytes = (uint32_t)Hq * (D * 2);
+  const uint32_t lane_off = (uint32_t)(kRows * ps + j) * row_bytes;
+  auto tile_rsrc = [&](const uint16_t *base, int qt) {
+    const int rows_left = min(nrows - qt * kQT, kQT);
+    const uint16_t *p =
+        base + (((int64_t)b * nrows + (int64_t)qt * kQT) * Hq + max(head, 0)) * D;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(p), 0,
+        (uint32_t)(rows_left - 1) * row_bytes + D * 2, kBufferWord3);
+  };
   uint4 qraw[8];
   auto load_q = [&](int qt) {
-    const int r = min(qt * kQT + kRows * ps + j, nrows - 1);
-    const uint16_t *qp =
-        q + (((int64_t)b * nrows + r) * Hq + max(head, 0)) * D + 8 * hh;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q, qt);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) qraw[c] = *(const uint4 *)(qp + 16 * c);
+    for (int c = 0; c < 8; ++c)
+      qraw[c] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rq, lane_off + 16u * hh + 32u * c, 0, 0));
   };
+  // Rows past the end (and padding heads) compute on valid clamped data;
+  // their outputs are never stored.
   bf16x8 qop[8];
-  auto make_qop = [&](bool act) {
+  auto make_qop = [&]() {
     const float *al = sm.ab[w % kGsize][0];
     const float *be = sm.ab[w % kGsize][1];
 #pragma unroll
@@ -139,8 +157,7 @@ __global__ __launch_bounds__(kNT, 2) void band_roll_kernel(
       for (int e = 0; e < 8; ++e) {
         const float qv = bf16_bits_to_f32((e & 1) ? (wv[e >> 1] >> 16)
                                                   : (wv[e >> 1] & 0xffffu));
-        qop[c][e] = act ? (__bf16)(al[d0 + e] * qv + be[d0 + e])
-                        : (__bf16)0.0f;
+        qop[c][e] = (__bf16)(al[d0 + e] * qv + be[d0 + e]);
       }
     }
   };
@@ -152,157 +169,152 @@ __global__ __launch_bounds__(kNT, 2) void band_roll_kernel(
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int Wm = W;
 
-  // ---- prologue: key tiles qt_begin-NTB+1 .. qt_begin, queries of qt_begin
-  for (int i = 0; i < NTB; ++i) {
-    const int kt = qt_begin - NTB + 1 + i;
-    if (kt < 0) continue;
-    load_kv(kt);
-    store_kv(kt % kSlots);
+  // ---- prologue: key tiles qt_begin-2 .. qt_begin, queries of qt_begin;
+  // tiles before the sequence start are zeros (finite, and masked out)
+  for (int i = 0; i < kSlots - 1; ++i) {
+    const int kt = qt_begin - (kSlots - 2) + i;
+    if (kt >= 0) {
+      load_kv(kt);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) kst[u] = vst[u] = make_uint4(0, 0, 0, 0);
+    }
+    store_kv(kt & (kSlots - 1));
   }
   load_q(qt_begin);
   __syncthreads();  // ring tiles and alpha/beta visible
-  {
-    const int r = qt_begin * kQT + kRows * ps + j;
-    make_qop(head >= 0 && r < nrows);
-  }
+  make_qop();
 
-  for (int qt = qt_begin; qt < qt_end; ++qt) {
-    const bool has_next = qt + 1 < qt_end;
-    if (has_next) {
-      load_kv(qt + 1);
-      load_q(qt + 1);
-    }
-    const int r_first = qt * kQT + kRows * ps;          // this wave's rows
+  // Sub-blocks of 32 keys: this wave's rows r_first .. r_first+31 need keys
+  // r_first-W+1 .. r_first+31, i.e. NSB sub-blocks ending with the one on the
+  // diagonal (global sub-block index 2 qt + ps).
+  f32x16 acc[4];
+  auto step = [&](int qt, int qt_next) {
+    const int r_first = qt * kQT + kRows * ps;
     const int rq = r_first + j;
-    const bool row_act = head >= 0 && rq < nrows;
-    float m = -INFINITY, l = 0.0f;
-    f32x16 acc[4], negm;
+    // keys lo .. rq of this lane's row
+    const int lo = max(rq - Wm + 1, 0);
+    const uint32_t span = (uint32_t)(rq - lo);
+    const int sb_first = 2 * qt + ps - (NSB - 1);
+    // S^T for every sub-block: independent MFMA chains
+    f32x16 s[NSB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NSB; ++i) {
+      const int sbg = sb_first + i;
+      const uint16_t *kp = &sm.k[(sbg >> 1) & (kSlots - 1)][32 * (sbg & 1) + j][8 * hh];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) negm[v] = 0.0f;
-
-#pragma unroll
-    for (int i = 0; i < NTB; ++i) {
-      const int kt = qt - NTB + 1 + i;
-      if (kt < 0) continue;  // before the sequence start (uniform)
-      const int slot = kt % kSlots;
-      // S^T - m
-      f32x16 s[2];
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk) {
-          const bf16x8 kop =
-              *(const bf16x8 *)&sm.k[slot][32 * sk + j][16 * c + 8 * hh];
-          s[sk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              kop, qop[c], c == 0 ? negm : s[sk], 0, 0, 0);
-        }
-      // band mask unless the tile lies inside every row's band (uniform per
-      // wave): key offset d = key - t kept iff -W < d <= 0, i.e.
-      // (unsigned)(d + W - 1) < W
-      const bool inside = kt * kBN >= r_first + kRows - W &&
-                          kt * kBN + kBN - 1 <= r_first;
-      if (!inside) {
-        const uint32_t u0 = (uint32_t)(kt * kBN - rq) + (uint32_t)(Wm - 1) +
-                            4u * hh;
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const uint32_t u =
-                u0 + (uint32_t)(32 * sk + 8 * (v >> 2) + (v & 3));
-            s[sk][v] = (u < (uint32_t)Wm) ? s[sk][v] : -INFINITY;
-          }
+      for (int c = 0; c < 8; ++c) {
+        const bf16x8 kop = *(const bf16x8 *)(kp + 16 * c);
+        s[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            kop, qop[c], c == 0 ? f32x16{} : s[i], 0, 0, 0);
       }
-      float tmax = -INFINITY;
+      // keep the operand reads of later sub-blocks from being hoisted
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next tile's queries arrive in the registers qop leaves free
+    load_q(qt_next);
+    // band mask on sub-blocks not inside every row's band (uniform per
+    // wave): key kept iff lo <= key <= rq, i.e. (unsigned)(key - lo) <= span
 #pragma unroll
-      for (int sk = 0; sk < 2; ++sk)
+    for (int i = 0; i < NSB; ++i) {
+      const int kb = 32 * (sb_first + i);
+      if (kb >= 0 && kb >= r_first + kRows - Wm && kb + 31 <= r_first)
+        continue;
+      const uint32_t u0 = (uint32_t)(kb - lo) + 4u * hh;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[sk][v]);
-      tmax = max_xor32(tmax);
-      const bool need = (m == -INFINITY) ? (tmax > -INFINITY) : (tmax > kTau);
-      if (__any(need)) {
-        const float shift = need ? tmax : 0.0f;
-        const float corr =
-            need ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(-shift))
-                 : 1.0f;
-        m = need ? ((m == -INFINITY) ? shift : m + shift) : m;
-        l *= corr;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
-#pragma unroll
-        for (int sk = 0; sk < 2; ++sk) s[sk] -= shift;
-        const float nm = (m == -INFINITY) ? 0.0f : -m;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) negm[v] = nm;
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t u = u0 + (uint32_t)(8 * (v >> 2) + (v & 3));
+        s[i][v] = (u <= span) ? s[i][v] : -INFINITY;
       }
-      bf16x8 pop[4];
+    }
+    // one row maximum over the whole band (it always holds the diagonal)
+    float m = -INFINITY;
 #pragma unroll
-      for (int kg = 0; kg < 4; ++kg) {
+    for (int i = 0; i < NSB; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) m = fmaxf(m, s[i][v]);
+    }
+    m = max_xor32(m);
+    // P = exp2(S - m), O^T += V^T P^T
+    float l = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NSB; ++i) {
+      const int sbg = sb_first + i;
+      const int slot = (sbg >> 1) & (kSlots - 1);
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+        bf16x8 pop;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pop[kg][e] = (__bf16)__builtin_amdgcn_exp2f(s[kg >> 1][8 * (kg & 1) + e]);
+          pop[e] = (__bf16)__builtin_amdgcn_exp2f(s[i][8 * kg + e] - m);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pop[kg][e], pop[kg][e + 1]};
+          const bf16x2 pr = {pop[e], pop[e + 1]};
           l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
         }
-      }
-#pragma unroll
-      for (int kg = 0; kg < 4; ++kg)
+        const int row = 32 * (sbg & 1) + 16 * kg + v_row0;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int row = 16 * kg + v_row0;
           const int col = 32 * dt + v_col0;
           const bf16x4 lo4 = lds_read_tr(&sm.v[slot][row][col]);
           const bf16x4 hi4 = lds_read_tr(&sm.v[slot][row + 8][col]);
           const bf16x8 vop = {lo4[0], lo4[1], lo4[2], lo4[3],
                               hi4[0], hi4[1], hi4[2], hi4[3]};
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[kg],
-                                                            acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop, acc[dt],
+                                                            0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-
-    // ---- output rows of this tile ------------------------------------------
+    // ---- output rows ---------------------------------------------------------
     l += __shfl_xor(l, 32, 64);
-    if (row_act) {
+    if (head >= 0) {
+      // Lane (j, hh) holds channels 32 dt + 8 q4 + 4 hh .. + 3. One
+      // v_permlane32_swap per word pairs the halves so that lane hh owns
+      // channels 32 dt + 16 qp + 8 hh .. + 7: one 16-byte store, 32
+      // contiguous bytes per row and instruction.
       const float inv = 1.0f / l;
-      uint16_t *op = o + (((int64_t)b * nrows + rq) * Hq + head) * D;
+      const __amdgpu_buffer_rsrc_t ro = tile_rsrc(o, qt);
+      auto pack = [&](int dt, int q4, int e) {
+        const uint32_t lo = __builtin_bit_cast(
+            uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e] * inv));
+        const uint32_t hi = __builtin_bit_cast(
+            uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e + 1] * inv));
+        return lo | (hi << 16);
+      };
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * dt + 8 * q4 + 4 * hh;
-          uint32_t pk[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const uint32_t lo = __builtin_bit_cast(
-                uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e] * inv));
-            const uint32_t hi = __builtin_bit_cast(
-                uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e + 1] * inv));
-            pk[e] = lo | (hi << 16);
-          }
-          *(uint2 *)(op + d0) = make_uint2(pk[0], pk[1]);
+        for (int qp = 0; qp < 2; ++qp) {
+          const auto x0 = __builtin_amdgcn_permlane32_swap(
+              pack(dt, 2 * qp, 0), pack(dt, 2 * qp + 1, 0), false, false);
+          const auto x1 = __builtin_amdgcn_permlane32_swap(
+              pack(dt, 2 * qp, 1), pack(dt, 2 * qp + 1, 1), false, false);
+          const u32x4 pk = {x0[0], x1[0], x0[1], x1[1]};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              pk, ro, lane_off + 16u * hh + 64u * dt + 32u * qp, 0, 0);
         }
     }
-    if (!has_next) break;
-    // The new key tile goes to the slot of tile qt-NTB, which no wave reads
-    // in this step; after the barrier every wave sees it.
-    store_kv((qt + 1) % kSlots);
-    {
-      const int r = (qt + 1) * kQT + kRows * ps + j;
-      make_qop(head >= 0 && r < nrows);
-    }
+  };
+
+  // The last step reloads its own tile into the unused slot (the loads are
+  // unconditional so that the staging registers never live across steps).
+  for (int qt = qt_begin; qt < qt_end; ++qt) {
+    const int qt_next = min(qt + 1, qt_end - 1);
+    load_kv(qt_next);
+    step(qt, qt_next);
+    if (qt + 1 == qt_end) break;
+    // The new key tile goes to the slot of tile qt-3, which no wave reads in
+    // this step; after the barrier every wave sees it.
+    store_kv((qt + 1) & (kSlots - 1));
+    make_qop();
     __syncthreads();
   }
 }
 
 }  // namespace
-
-int band_roll_tiles(int W) { return (W - 1 + kBN - 1) / kBN + 1; }
 
 hipError_t launch_band_roll(const void *q, const float *alpha,
                             const float *beta, const void *k_cache,
@@ -325,17 +337,21 @@ hipError_t launch_band_roll(const void *q, const float *alpha,
   const int seg_len = (int)((n_qtiles + n_segs - 1) / n_segs);
   n_segs = (n_qtiles + seg_len - 1) / seg_len;
   const dim3 grid((unsigned)(n_segs * per));
-  const int ntb = band_roll_tiles(W);
+  if (W < 1 || W > kRollMaxWindow) return hipErrorInvalidValue;
+  const int nsb = (W - 1 + 31) / 32 + 1;  // 32-key sub-blocks per row block
 #define ORTHROS_ROLL(N)                                                      \
   hipLaunchKernelGGL(band_roll_kernel<N>, grid, dim3(kNT), 0, stream,        \
                      (const uint16_t *)q, alpha, beta,                       \
                      (const uint16_t *)k_cache, (const uint16_t *)v_cache,   \
                      (uint16_t *)o, nrows, Hq, n_kv, cap, W, n_qtiles,       \
                      seg_len, (int)n_segs, groups)
-  if (ntb == 3)
-    ORTHROS_ROLL(3);
-  else
-    return hipErrorInvalidValue;
+  switch (nsb) {
+    case 1: ORTHROS_ROLL(1); break;
+    case 2: ORTHROS_ROLL(2); break;
+    case 3: ORTHROS_ROLL(3); break;
+    case 4: ORTHROS_ROLL(4); break;
+    default: ORTHROS_ROLL(5); break;
+  }
 #undef ORTHROS_ROLL
   return hipGetLastError();
 }

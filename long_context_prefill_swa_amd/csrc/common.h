@@ -98,9 +98,8 @@ hipError_t launch_band_mfma(const void *q, const float *alpha,
                             hipStream_t stream);
 
 // Rolling-window attention for small windows, bf16, D = 128, 4 query heads
-// per KV head, rows at positions 0 .. nrows-1: key tiles per query tile
-// band_roll_tiles(W) must be 3 (65 < W <= 129).
-int band_roll_tiles(int W);
+// per KV head, rows at positions 0 .. nrows-1, 1 <= W <= kRollMaxWindow.
+constexpr int kRollMaxWindow = 129;
 hipError_t launch_band_roll(const void *q, const float *alpha,
                             const float *beta, const void *k_cache,
                             const void *v_cache, void *o, int B, int nrows,

@@ -259,7 +259,7 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
     return fail(ORTHROS_EINVAL, "tensor size overflows");
   hipError_t e;
   if (mfma_eligible(dtype, D, T, {q_pre, alpha, beta, k_cache, v_cache, o}) &&
-      groups.gsize == 4 && band_roll_tiles(W) == 3) {
+      groups.gsize == 4 && W <= kRollMaxWindow) {
     // small window: the pass streams Q/O through HBM (rolling kernel)
     e = launch_band_roll(q_pre, alpha, beta, k_cache, v_cache, o, B, T, Hq,
                          cap, W, groups, Hkv, as_stream(stream));

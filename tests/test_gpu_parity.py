@@ -116,8 +116,8 @@ def test_swa_bf16_parity(B, T, Hq, Hkv, W):
     compare(o, oracle_swa(q, a, b, k, v, W), dt, "swa")
 
 
-# --- base stream: rolling-window kernel (4 query heads per KV head, three
-# key tiles per query tile: 65 < W <= 129) ------------------------------------
+# --- base stream: rolling-window kernel (4 query heads per KV head,
+# W <= 129) --------------------------------------------------------------------
 
 @pytest.mark.parametrize("B,T,Hq,Hkv,W", [
     (2, 1000, 8, 2, 128),   # the trained window, ragged tail
@@ -125,6 +125,13 @@ def test_swa_bf16_parity(B, T, Hq, Hkv, W):
     (1, 576, 8, 2, 129),    # largest; T a multiple of the tile
     (1, 513, 32, 8, 100),   # eight groups, one row past a tile
     (2, 63, 8, 2, 128),     # a single partial tile
+    (1, 333, 8, 2, 2),      # one to five 32-key sub-blocks per row block
+    (1, 333, 8, 2, 32),
+    (1, 333, 8, 2, 33),
+    (1, 333, 8, 2, 64),
+    (1, 333, 8, 2, 96),
+    (1, 333, 8, 2, 97),
+    (1, 333, 8, 2, 98),
 ])
 def test_swa_rolling_parity(B, T, Hq, Hkv, W):
     D = 128
