@@ -50,6 +50,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
 }
 
 constexpr int kSlots = 4;  // ring of key tiles: the band's three + the next
+constexpr int kOutStride = 136;              // bytes per staged output row
+constexpr int kOutRegion = kRows * kOutStride;  // per wave: 4352 bytes
+static_assert(kGsize * kOutRegion <= kBN * kKS * 2, "output staging fits a K slot");
 
 struct RollSmem {
   uint16_t k[kSlots][kBN][kKS];
@@ -268,34 +271,54 @@ __global__ __launch_bounds__(kNT, 2) void band_roll_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // ---- output rows ---------------------------------------------------------
+    // ---- output rows, staged through LDS ------------------------------------
+    // Once every wave is past its PV products, the ring slot of tile qt-2
+    // is free (the next step's band starts at qt-1). Each wave takes a
+    // private 32 x 64-channel region of it (136-byte rows) and writes O in
+    // two channel halves: fragments in, then whole 128-byte row pieces out
+    // (8 lanes per row, 16 bytes each), so every store covers full lines.
     l += __shfl_xor(l, 32, 64);
+    __syncthreads();
     if (head >= 0) {
-      // Lane (j, hh) holds channels 32 dt + 8 q4 + 4 hh .. + 3. One
-      // v_permlane32_swap per word pairs the halves so that lane hh owns
-      // channels 32 dt + 16 qp + 8 hh .. + 7: one 16-byte store, 32
-      // contiguous bytes per row and instruction.
       const float inv = 1.0f / l;
+      const int fslot = (qt + 2) & (kSlots - 1);
+      uint8_t *region =
+          (ps == 0 ? (uint8_t *)&sm.k[fslot][0][0] : (uint8_t *)&sm.v[fslot][0][0]) +
+          (w % kGsize) * kOutRegion;
       const __amdgpu_buffer_rsrc_t ro = tile_rsrc(o, qt);
-      auto pack = [&](int dt, int q4, int e) {
-        const uint32_t lo = __builtin_bit_cast(
-            uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e] * inv));
-        const uint32_t hi = __builtin_bit_cast(
-            uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e + 1] * inv));
-        return lo | (hi << 16);
-      };
+      const int rr = lane >> 3, cc = lane & 7;  // read-back row / chunk
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int qp = 0; qp < 2; ++qp) {
-          const auto x0 = __builtin_amdgcn_permlane32_swap(
-              pack(dt, 2 * qp, 0), pack(dt, 2 * qp + 1, 0), false, false);
-          const auto x1 = __builtin_amdgcn_permlane32_swap(
-              pack(dt, 2 * qp, 1), pack(dt, 2 * qp + 1, 1), false, false);
-          const u32x4 pk = {x0[0], x1[0], x0[1], x1[1]};
-          __builtin_amdgcn_raw_buffer_store_b128(
-              pk, ro, lane_off + 16u * hh + 64u * dt + 32u * qp, 0, 0);
+        for (int d2 = 0; d2 < 2; ++d2) {
+          const int dt = 2 * half + d2;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            uint32_t pk[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const uint32_t lo = __builtin_bit_cast(
+                  uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e] * inv));
+              const uint32_t hi = __builtin_bit_cast(
+                  uint16_t, (__bf16)(acc[dt][4 * q4 + 2 * e + 1] * inv));
+              pk[e] = lo | (hi << 16);
+            }
+            *(uint2 *)(region + j * kOutStride + 64 * d2 + 16 * q4 + 8 * hh) =
+                make_uint2(pk[0], pk[1]);
+          }
         }
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int r = rr + 8 * it;
+          const uint8_t *src = region + r * kOutStride + 16 * cc;
+          const uint2 a0 = *(const uint2 *)src;
+          const uint2 a1 = *(const uint2 *)(src + 8);
+          const u32x4 pk = {a0.x, a0.y, a1.x, a1.y};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              pk, ro, (uint32_t)(kRows * ps + r) * row_bytes + 128u * half +
+                          16u * cc, 0, 0);
+        }
+      }
     }
   };
 
