@@ -15,9 +15,9 @@
  *
  * K/V come from the base stream only and form the full per-layer cache that
  * both streams read; the output stream never writes K/V (reproduction note
- * "Orthros：阶段异构注意力", background section). The library takes the
- * projected, pre-affine queries and the projected K/V; the projections and
- * W_O are the caller's.
+ * "Orthros：阶段异构注意力", background section). The attention entry
+ * points take the projected, pre-affine queries and the projected K/V;
+ * orthros_layer_forward also runs the projections and W_O.
  *
  * Conventions shared by every entry point
  * ----------------------------------------
@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 2
+#define ORTHROS_ABI_VERSION 3
 
 /* dtype codes */
 #define ORTHROS_F32 0
@@ -273,6 +273,56 @@ int orthros_decode_pair_paged(const void *q_pre, const void *qx_pre,
                               int64_t max_len_after, int W,
                               const int32_t *head_map, int dtype, void *ws,
                               size_t ws_bytes, void *stream);
+
+/*
+ * orthros_layer_forward - one Orthros attention layer, projections included.
+ *
+ * Pages: paper text §3.1 (k_i = x_i W_K, v_i = x_i W_V for the T base
+ * tokens; q_i = alpha (.) (x_i W_Q) + beta for every base token and
+ * q'_i = alpha' (.) (x'_i W_Q) + beta' for the T_out output-specific tokens,
+ * one shared W_Q) and its description of Algorithm 1 and Figure 1(b): the
+ * input is the T base rows followed by the T_out output rows, and the
+ * outputs of the two streams, in that same row order, go through W_O.
+ *
+ * For every batch entry b (T_in = T - T_out, output row r at position
+ * T_in + r):
+ *   Q    = x[b] W_Q                      all T + T_out rows
+ *   K, V = x[b, 0..T-1] W_K, W_V         written to cache rows 0..T-1,
+ *                                        then cache_len[b] = T
+ *   o    = sliding window (W) of the base queries      rows 0..T-1
+ *   o'   = global cross-attention of the output queries rows T..T+T_out-1
+ *   y[b] = [o; o'] W_O
+ * Projections are hipBLASLt GEMMs (bf16 operands, fp32 accumulation, bf16
+ * results); every intermediate (Q, K, V, o) is rounded to bf16, as in the
+ * other entry points. Query heads map to KV heads contiguously (h / (Hq/Hkv)).
+ *
+ *   x           [dev] [B, T + T_out, d_model] bf16
+ *   w_q         [dev] [d_model, Hq*D] bf16 (row-major: x W_Q)
+ *   w_k, w_v    [dev] [d_model, Hkv*D] bf16
+ *   w_o         [dev] [Hq*D, d_model] bf16
+ *   alpha, beta, alpha_x, beta_x [dev] fp32 [Hq*D] (the _x pair may be NULL
+ *               when T_out = 0)
+ *   k_cache, v_cache [dev] [B, Hkv, cap, D] bf16, rows 0..T-1 written
+ *   cache_len   [dev] int32[B], set to T (whatever it held before)
+ *   y           [dev] [B, T + T_out, d_model] bf16, written
+ *   ws, ws_bytes [dev] scratch of orthros_layer_workspace_bytes(...) bytes
+ *               (intermediates of one batch entry plus GEMM workspace)
+ * 1 <= T, 0 <= T_out <= T, cap >= T, W >= 1, Hq a multiple of Hkv.
+ * Errors: EINVAL, EUNSUPPORTED (D), EWORKSPACE, EHIP (also a failing
+ * hipBLASLt call). The first call on a device creates that device's
+ * hipBLASLt handle, kept until the process ends.
+ */
+int orthros_layer_forward(const void *x, const void *w_q, const void *w_k,
+                          const void *w_v, const void *w_o, const float *alpha,
+                          const float *beta, const float *alpha_x,
+                          const float *beta_x, void *k_cache, void *v_cache,
+                          int32_t *cache_len, void *y, int B, int T, int T_out,
+                          int d_model, int Hq, int Hkv, int D, int64_t cap,
+                          int W, void *ws, size_t ws_bytes, void *stream);
+
+/* Scratch bytes orthros_layer_forward needs (0 for invalid sizes). */
+size_t orthros_layer_workspace_bytes(int B, int T, int T_out, int d_model,
+                                     int Hq, int Hkv, int D);
 
 /*
  * Scratch bytes needed by orthros_global_xattn (op ORTHROS_OP_GLOBAL_XATTN,

@@ -68,6 +68,10 @@ def lib():
                                             vp, vp, i64, i32, vp, i32, vp,
                                             vp, vp, i32, i32, i32, i32, i64,
                                             i32, vp, i32, vp, sz, vp]
+    L.orthros_layer_forward.argtypes = [vp] * 13 + [i32] * 7 + [i64, i32, vp,
+                                                                sz, vp]
+    L.orthros_layer_workspace_bytes.argtypes = [i32] * 7
+    L.orthros_layer_workspace_bytes.restype = sz
     L.orthros_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i64]
     L.orthros_workspace_bytes.restype = sz
     L.orthros_strerror.argtypes = [i32]
@@ -296,6 +300,44 @@ def orthros_decode_pair_paged(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
         _dtype_code(q_pre), _dev(ws, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream, q_pre)))
+
+
+def orthros_layer_workspace_bytes(B, T, T_out, d_model, Hq, Hkv, D):
+    return int(lib().orthros_layer_workspace_bytes(B, T, T_out, d_model, Hq,
+                                                   Hkv, D))
+
+
+def orthros_layer_forward(x, w_q, w_k, w_v, w_o, alpha, beta, alpha_x,
+                          beta_x, k_cache, v_cache, cache_len, y, T_out, W,
+                          ws=None, stream=None):
+    """x, y [B, T+T_out, d_model]; w_q [d_model, Hq*D]; w_k, w_v
+    [d_model, Hkv*D]; w_o [Hq*D, d_model]; caches [B, Hkv, cap, D]."""
+    B, M, d_model = x.shape
+    T = M - int(T_out)
+    Hkv, cap, D = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+    Hq = w_q.shape[1] // D
+    if tuple(k_cache.shape) != (B, Hkv, cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, Hkv, cap, D]")
+    if (tuple(w_q.shape) != (d_model, Hq * D) or
+            tuple(w_k.shape) != (d_model, Hkv * D) or w_v.shape != w_k.shape or
+            tuple(w_o.shape) != (Hq * D, d_model)):
+        raise ValueError("weights must be [d_model, Hq*D], [d_model, Hkv*D] "
+                         "x2 and [Hq*D, d_model]")
+    if y.shape != x.shape:
+        raise ValueError("y must have x's shape")
+    if ws is None:
+        ws = workspace(orthros_layer_workspace_bytes(B, T, int(T_out), d_model,
+                                                     Hq, Hkv, D), x.device)
+    bf = torch.bfloat16
+    f32 = torch.float32
+    _check(lib().orthros_layer_forward(
+        _dev(x, "x", bf), _dev(w_q, "w_q", bf), _dev(w_k, "w_k", bf),
+        _dev(w_v, "w_v", bf), _dev(w_o, "w_o", bf), _dev(alpha, "alpha", f32),
+        _dev(beta, "beta", f32), _dev(alpha_x, "alpha_x", f32),
+        _dev(beta_x, "beta_x", f32), _dev(k_cache, "k_cache", bf),
+        _dev(v_cache, "v_cache", bf), _dev(cache_len, "cache_len", torch.int32),
+        _dev(y, "y", bf), B, T, int(T_out), d_model, Hq, Hkv, D, cap, int(W),
+        _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream, x)))
 
 
 def orthros_check_device_errors(stream=None, device=None):

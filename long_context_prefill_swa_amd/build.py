@@ -17,7 +17,8 @@ LIB = os.path.join(HERE, "liborthros.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kv_append.hip", "rowwise.hip", "splitkv_mfma.hip",
-           "band_mfma.hip", "band_roll.hip", "orthros_api.cpp"]
+           "band_mfma.hip", "band_roll.hip", "orthros_api.cpp", "gemm.cpp",
+           "layer.cpp"]
 
 # Packed fp32 instructions stay off: hipcc is asked not to form them.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -46,7 +47,8 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

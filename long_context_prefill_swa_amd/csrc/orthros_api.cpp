@@ -168,6 +168,14 @@ void fill_ws(SplitKVArgs *a, void *ws, const SplitPlan &p, int B,
 
 }  // namespace
 
+namespace orthros {
+// Records a message for orthros_last_error (used by the layer entry point).
+int api_error(int code, const char *msg) {
+  snprintf(g_msg, sizeof(g_msg), "%s", msg);
+  return code;
+}
+}  // namespace orthros
+
 extern "C" {
 
 int orthros_abi_version(void) { return ORTHROS_ABI_VERSION; }

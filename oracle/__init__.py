@@ -16,6 +16,12 @@ names the passage of the pages it follows:
 * ``row_weights`` normalised weights of one row (support / sum checks)
 * ``Cache``       incremental prefill-then-decode, the decode pair step
                   (same page, §3.2 Decoding)
+* ``layer``       one attention layer with its projections: k, v = x W_K,
+                  x W_V for the base rows, q = alpha (.) (x W_Q) + beta and
+                  q' = alpha' (.) (x' W_Q) + beta', the two streams, their
+                  outputs in input row order, then W_O (same page, §3.1,
+                  the description of Algorithm 1 and Figure 1(b)); numpy
+                  fp64 matrix products, attention through ``swa``/``xattn``
 
 Parity pins (tests/test_oracle_pins.py) tie every function to something
 other than itself: torch's scaled_dot_product_attention for the cases that
@@ -213,3 +219,46 @@ class Cache:
         if rc:
             raise ValueError("oracle decode_pair: invalid arguments")
         return o, o_x
+
+
+def layer(x, w_q, w_k, w_v, w_o, alpha, beta, alpha_x, beta_x, T_out, W,
+          Hkv, D, rows=None):
+    """One Orthros attention layer, fp64.
+
+    x [B, T + T_out, d_model]: the T base rows, then the T_out
+    output-specific rows (row T + r is the output token at position
+    T_in + r, T_in = T - T_out). Weights as in x W: w_q [d_model, Hq*D],
+    w_k, w_v [d_model, Hkv*D], w_o [Hq*D, d_model].
+    Returns y [B, T + T_out, d_model], or with `rows` (row indices into the
+    T + T_out rows) y[:, rows] only; a base row t is then evaluated over its
+    key slice [max(0, t-W+1), t] and an output row over [0, T_in + r].
+    """
+    x = _f64(x)
+    w_q, w_k, w_v, w_o = (_f64(w) for w in (w_q, w_k, w_v, w_o))
+    B, M, _ = x.shape
+    T = M - T_out
+    T_in = T - T_out
+    Hq = w_q.shape[1] // D
+    k = (x[:, :T] @ w_k).reshape(B, T, Hkv, D)
+    v = (x[:, :T] @ w_v).reshape(B, T, Hkv, D)
+    if rows is None:
+        q_all = (x @ w_q).reshape(B, M, Hq, D)
+        o, _ = swa(q_all[:, :T], alpha, beta, k, v, W)
+        parts = [o]
+        if T_out:
+            ox, _ = xattn(q_all[:, T:], alpha_x, beta_x, k, v, T_in)
+            parts.append(ox)
+        o_cat = np.concatenate(parts, axis=1).reshape(B, M, Hq * D)
+        return o_cat @ w_o
+    out = []
+    for i in rows:
+        q_i = (x[:, i] @ w_q).reshape(B, 1, Hq, D)
+        if i < T:
+            lo = max(0, i - W + 1)
+            o_i, _ = xattn(q_i, alpha, beta, k[:, lo:i + 1], v[:, lo:i + 1],
+                           i - lo)
+        else:
+            t = T_in + (i - T)
+            o_i, _ = xattn(q_i, alpha_x, beta_x, k[:, :t + 1], v[:, :t + 1], t)
+        out.append(o_i.reshape(B, Hq * D) @ w_o)
+    return np.stack(out, axis=1)

@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("orthros_kv_append", "orthros_swa_prefill",
               "orthros_global_xattn", "orthros_decode_pair",
-              "orthros_kv_append_paged", "orthros_decode_pair_paged"):
+              "orthros_kv_append_paged", "orthros_decode_pair_paged",
+              "orthros_layer_forward", "orthros_layer_workspace_bytes"):
         assert n in names
 
 
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.orthros_abi_version() == 2
+    assert L.orthros_abi_version() == 3
     for code in (OK, EINVAL, EUNSUP, ECAP, EWS, EHIP):
         assert L.orthros_strerror(code)
     assert b"unknown" in L.orthros_strerror(42)
@@ -235,3 +236,43 @@ def test_decode_pair_paged_workspace_matches_contiguous(L):
     assert need > 0
     assert paged_decode(L, ws=FAKE, ws_bytes=need - 16) == EWS
     assert paged_decode(L, B=0) == OK
+
+
+def layer(L, ws_bytes=None, **kw):
+    a = dict(B=1, T=64, T_out=1, d_model=256, Hq=4, Hkv=2, D=128, cap=64,
+             W=16, x=FAKE, y=FAKE)
+    a.update(kw)
+    need = L.orthros_layer_workspace_bytes(a["B"], a["T"], a["T_out"],
+                                           a["d_model"], a["Hq"], a["Hkv"],
+                                           a["D"])
+    return L.orthros_layer_forward(
+        a["x"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        FAKE, a["y"], a["B"], a["T"], a["T_out"], a["d_model"], a["Hq"],
+        a["Hkv"], a["D"], a["cap"], a["W"], FAKE,
+        need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(T_out=65), EINVAL, "T_out"),
+    (dict(T=0), EINVAL, "T_out"),
+    (dict(d_model=0), EINVAL, "d_model"),
+    (dict(Hq=6, Hkv=4), EINVAL, "heads"),
+    (dict(D=15), EUNSUP, "head dimension"),
+    (dict(W=0), EINVAL, "window"),
+    (dict(cap=63), EINVAL, "cap"),
+    (dict(x=None), EINVAL, "null"),
+    (dict(y=None), EINVAL, "null"),
+    (dict(ws_bytes=1000), EWS, "workspace"),
+])
+def test_layer_forward_rejects(L, kw, code, needle):
+    assert layer(L, **kw) == code
+    assert needle in last(L)
+
+
+def test_layer_workspace_covers_the_intermediates(L):
+    T, T_out, Hq, Hkv, D = 1000, 3, 8, 2, 128
+    need = L.orthros_layer_workspace_bytes(1, T, T_out, 512, Hq, Hkv, D)
+    inter = 2 * ((T + T_out) * Hq * D * 2) + 2 * (T * Hkv * D * 2)
+    assert need >= inter + (64 << 20)
+    assert L.orthros_layer_workspace_bytes(1, 10, 11, 512, Hq, Hkv, D) == 0
+    assert layer(L, B=0) == OK

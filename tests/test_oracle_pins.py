@@ -409,3 +409,82 @@ def test_invalid_arguments_raise():
     with pytest.raises(ValueError):
         oracle.swa(q, np.ones(8), np.zeros(8), k, k, 2,
                    head_map=np.array([0, 1], dtype=np.int32))     # map >= Hkv
+
+
+# --- the layer with its projections (oracle.layer) ---------------------------
+
+def torch_layer(x, w_q, w_k, w_v, w_o, a, b, ax, bx, T_out, W, Hkv, D):
+    """Independent fp64 evaluation of one layer: torch matmuls, the affine
+    written out, and scaled_dot_product_attention with triangular band masks
+    (base rows) and causal rows (output rows)."""
+    X = torch.from_numpy(x).double()
+    B, M, _ = X.shape
+    T = M - T_out
+    Hq = w_q.shape[1] // D
+    t = lambda z: torch.from_numpy(np.ascontiguousarray(z)).double()  # noqa
+    q_all = X @ t(w_q)
+    q = t(a) * q_all[:, :T] + t(b)
+    k = (X[:, :T] @ t(w_k)).reshape(B, T, Hkv, D).numpy()
+    v = (X[:, :T] @ t(w_v)).reshape(B, T, Hkv, D).numpy()
+    o = sdpa(q.reshape(B, T, Hq, D).numpy(), k, v, mask=band_mask(T, W))
+    parts = [o]
+    if T_out:
+        qx = (t(ax) * q_all[:, T:] + t(bx)).reshape(B, T_out, Hq, D).numpy()
+        rows = band_mask(T, T, q_offset=T - T_out)   # causal rows T_in..T-1
+        parts.append(sdpa(qx, k, v, mask=rows))
+    o_cat = np.concatenate(parts, axis=1).reshape(B, M, Hq * D)
+    return o_cat @ w_o
+
+
+def layer_case(B, T, T_out, dm, Hq, Hkv, D, seed):
+    x = rnd((B, T + T_out, dm), seed)
+    w = [rnd(s, seed + i + 1, 1 / math.sqrt(s[0])) for i, s in
+         enumerate([(dm, Hq * D), (dm, Hkv * D), (dm, Hkv * D), (Hq * D, dm)])]
+    a, b = 1 + 0.1 * rnd(Hq * D, seed + 5), 0.1 * rnd(Hq * D, seed + 6)
+    ax, bx = 1 + 0.1 * rnd(Hq * D, seed + 7), 0.1 * rnd(Hq * D, seed + 8)
+    return x, w, (a, b, ax, bx)
+
+
+@pytest.mark.parametrize("B,T,T_out,dm,Hq,Hkv,D,W", [
+    (2, 30, 3, 24, 4, 2, 8, 7),
+    (1, 40, 40, 16, 2, 1, 8, 5),     # every position also an output row (PT)
+    (1, 25, 0, 16, 2, 2, 8, 100),    # no output rows; W above T
+    (2, 33, 1, 32, 4, 4, 8, 1),      # window of one
+])
+def test_layer_equals_masked_attention_with_projections(B, T, T_out, dm, Hq,
+                                                         Hkv, D, W):
+    x, w, aff = layer_case(B, T, T_out, dm, Hq, Hkv, D, 300 + T)
+    got = oracle.layer(x, *w, *aff, T_out, W, Hkv, D)
+    ref = torch_layer(x, *w, *aff, T_out, W, Hkv, D)
+    assert got.shape == (B, T + T_out, dm)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_rows_mode_equals_full_mode():
+    B, T, T_out, dm, Hq, Hkv, D, W = 2, 50, 4, 16, 4, 2, 8, 9
+    x, w, aff = layer_case(B, T, T_out, dm, Hq, Hkv, D, 401)
+    full = oracle.layer(x, *w, *aff, T_out, W, Hkv, D)
+    rows = [0, 1, 8, 9, 10, 49, 50, 53]
+    part = oracle.layer(x, *w, *aff, T_out, W, Hkv, D, rows=rows)
+    np.testing.assert_allclose(part, full[:, rows], rtol=1e-12, atol=1e-13)
+
+
+def test_layer_output_row_order_and_causality():
+    """Output rows depend only on their own hidden row and on base rows up
+    to their position; base rows never see the output rows."""
+    B, T, T_out, dm, Hq, Hkv, D, W = 1, 20, 3, 16, 2, 1, 8, 6
+    x, w, aff = layer_case(B, T, T_out, dm, Hq, Hkv, D, 501)
+    y0 = oracle.layer(x, *w, *aff, T_out, W, Hkv, D)
+    x1 = x.copy()
+    x1[:, T + 1] += 1.0                      # output row of position T_in+1
+    y1 = oracle.layer(x1, *w, *aff, T_out, W, Hkv, D)
+    changed = np.abs(y1 - y0).max(axis=(0, 2)) > 0
+    assert changed.tolist() == [i == T + 1 for i in range(T + T_out)]
+    x2 = x.copy()
+    x2[:, T - 1] += 1.0                      # the last base row (position T-1)
+    y2 = oracle.layer(x2, *w, *aff, T_out, W, Hkv, D)
+    changed = np.abs(y2 - y0).max(axis=(0, 2)) > 0
+    T_in = T - T_out
+    expect = [T - 1 <= i < T or i == T + T_out - 1
+              for i in range(T + T_out)]
+    assert changed.tolist() == expect, (changed, T_in)

@@ -11,6 +11,10 @@ Recipe (the same for every configuration):
   * alpha, alpha': 1 + 0.1 * N(0, 1); beta, beta': 0.1 * N(0, 1); fp32, one
     value per channel of the Hq*D query projection.
   * The 1/sqrt(D) softmax scale is part of the method, not of the inputs.
+  * Layer forward: hidden rows x ~ N(0, 1) ([B, T + T_out, d_model], the T
+    base rows then the T_out output rows, drawn independently); weights
+    N(0, 1) / sqrt(fan_in), then rounded to bf16, so every projection has
+    unit variance. d_model = Hq * D unless stated.
 The pages' efficiency workloads are length-only (128K input / short
 output); these configurations stand in for them with synthetic tensors.
 """
@@ -72,7 +76,8 @@ def workload(name: str):
 
 # Tensor ids inside a configuration's seed space.
 _TID = {"q_pre": 1, "qx_pre": 2, "k": 3, "v": 4, "alpha": 5, "beta": 6,
-        "alpha_x": 7, "beta_x": 8}
+        "alpha_x": 7, "beta_x": 8, "x": 9, "w_q": 10, "w_k": 11, "w_v": 12,
+        "w_o": 13}
 
 
 def seed_of(cfg_id: int, tensor: str, step: int = 0) -> int:
@@ -170,3 +175,42 @@ def decode_all_steps(cfg: Config, cfg_id: int, steps: Optional[int] = None,
         qx_pre=normal((n, B, Hq, D), s("qx_pre"), dt, device),
         k_new=normal((n, B, Hkv, D), s("k"), dt, device),
         v_new=normal((n, B, Hkv, D), s("v"), dt, device))
+
+
+@dataclass
+class LayerInputs:
+    x: torch.Tensor        # [B, T + T_out, d_model] bf16
+    w_q: torch.Tensor      # [d_model, Hq*D]
+    w_k: torch.Tensor      # [d_model, Hkv*D]
+    w_v: torch.Tensor      # [d_model, Hkv*D]
+    w_o: torch.Tensor      # [Hq*D, d_model]
+    alpha: torch.Tensor
+    beta: torch.Tensor
+    alpha_x: torch.Tensor
+    beta_x: torch.Tensor
+
+
+def scaled_normal(shape, seed: int, fan_in: int, dtype, device="cpu"):
+    """N(0, 1) / sqrt(fan_in), drawn in fp32, then rounded to `dtype`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    w = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    return (w * fan_in ** -0.5).to(dtype)
+
+
+def layer_inputs(cfg: Config, cfg_id: int, d_model: Optional[int] = None,
+                 device="cpu") -> LayerInputs:
+    """Inputs of one layer forward: hidden rows, the four weights, the
+    affine vectors (bf16 tensors, fp32 affine)."""
+    dm = cfg.Hq * cfg.D if d_model is None else d_model
+    s = lambda name: seed_of(cfg_id, name)  # noqa: E731
+    bf = torch.bfloat16
+    HqD, HkvD = cfg.Hq * cfg.D, cfg.Hkv * cfg.D
+    a, b, ax, bx = affine_inputs(cfg, cfg_id, device)
+    return LayerInputs(
+        x=normal((cfg.B, cfg.T + cfg.T_out, dm), s("x"), bf, device),
+        w_q=scaled_normal((dm, HqD), s("w_q"), dm, bf, device),
+        w_k=scaled_normal((dm, HkvD), s("w_k"), dm, bf, device),
+        w_v=scaled_normal((dm, HkvD), s("w_v"), dm, bf, device),
+        w_o=scaled_normal((HqD, dm), s("w_o"), HqD, bf, device),
+        alpha=a, beta=b, alpha_x=ax, beta_x=bx)
