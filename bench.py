@@ -13,10 +13,14 @@ The reported value is prefill tokens/s (B*T over the summed time of the
 three prefill launches); the decode pair's KV GB/s and latency, the full
 causal run at the same T (speedup ratio), the roofline of the dominant
 kernel and the fp64 CPU oracle's rate on a bounded sample are reported
-beside it. All GPU times come from HIP events on the launch stream.
+beside it, with the sliding window at W = 128, the paged ragged decode and
+the whole layer (projections + attention + W_O) at 128K as extra legs
+outside the timed steps. All GPU times come from HIP events on the launch
+stream.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-causal]
-                [--no-cpu-baseline] [--only prefill|decode]
+                [--no-paged] [--no-layer] [--no-cpu-baseline]
+                [--only prefill|decode]
 """
 import argparse
 import hashlib
@@ -80,6 +84,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-causal", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     args = ap.parse_args()
@@ -300,6 +305,11 @@ def main():
         log(f"[bench] swa W=128: {t_s:.3f} ms, "
             f"{out['swa_w128']['gbps']:.0f} GB/s")
 
+    # ---- the whole layer: projections + both streams + W_O (128K) -----------
+    if run_prefill and not args.no_layer:
+        out["layer_forward"] = layer_forward_leg(lo, pc, pc_id, kc4, vc4, dev,
+                                                 ev)
+
     # ---- paged cache, ragged lengths (variable-length batched decoding) -----
     if run_decode and not args.no_paged:
         del kc3, vc3
@@ -312,6 +322,44 @@ def main():
         out["cpu_baseline"] = cpu_baseline(px, pc)
 
     print(json.dumps(out), flush=True)
+
+
+def layer_forward_leg(lo, pc, pc_id, kc, vc, dev, ev, reps=2):
+    """One Orthros layer at the 128K prefill shape (d_model = Hq*D = 4096,
+    one output row): hipBLASLt projections, cache fill, both attention
+    streams and W_O, at the configuration's window and at W = 128."""
+    import torch
+
+    from workloads import layer_inputs
+    x = layer_inputs(pc, pc_id, None, dev)
+    B, M, dm = x.x.shape
+    cl = torch.zeros(B, dtype=torch.int32, device=dev)
+    y = torch.empty_like(x.x)
+    ws = lo.workspace(lo.orthros_layer_workspace_bytes(
+        B, pc.T, pc.T_out, dm, pc.Hq, pc.Hkv, pc.D), dev)
+    HqD, HkvD = pc.Hq * pc.D, pc.Hkv * pc.D
+    gemm_flop = 2.0 * B * (M * dm * HqD * 2 + pc.T * dm * HkvD * 2)
+    res = {"d_model": dm, "gemm_tflop": gemm_flop / 1e12}
+    for W in (pc.W, 128):
+        def f():
+            lo.orthros_layer_forward(x.x, x.w_q, x.w_k, x.w_v, x.w_o, x.alpha,
+                                     x.beta, x.alpha_x, x.beta_x, kc, vc, cl,
+                                     y, pc.T_out, W, ws=ws)
+        f()
+        torch.cuda.synchronize()
+        e0 = ev()
+        for _ in range(reps):
+            f()
+        e1 = ev()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps
+        res[f"W{W}"] = {"ms": t, "tokens_per_s": B * pc.T / (t * 1e-3)}
+        log(f"[bench] layer W={W}: {t:.2f} ms, "
+            f"{B * pc.T / (t * 1e-3) / 1e6:.2f} M tokens/s")
+    lo.orthros_check_device_errors()
+    del x, y, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def paged_ragged_decode(lo, dc, dc_id, st, a, b, ax, bx, dev, ev,
