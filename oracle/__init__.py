@@ -16,6 +16,9 @@ names the passage of the pages it follows:
 * ``row_weights`` normalised weights of one row (support / sum checks)
 * ``Cache``       incremental prefill-then-decode, the decode pair step
                   (same page, §3.2 Decoding)
+* ``attn_backward`` gradients of both streams (q_pre, qx_pre, K, V and the
+                  four scale-offset vectors) for training (paper text §3.2,
+                  pre-training and SFT), row by row in numpy fp64
 * ``layer``       one attention layer with its projections: k, v = x W_K,
                   x W_V for the base rows, q = alpha (.) (x W_Q) + beta and
                   q' = alpha' (.) (x' W_Q) + beta', the two streams, their
@@ -262,3 +265,70 @@ def layer(x, w_q, w_k, w_v, w_o, alpha, beta, alpha_x, beta_x, T_out, W,
             o_i, _ = xattn(q_i, alpha_x, beta_x, k[:, :t + 1], v[:, :t + 1], t)
         out.append(o_i.reshape(B, Hq * D) @ w_o)
     return np.stack(out, axis=1)
+
+
+def attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k, v, d_o,
+                  d_ox, W, head_map=None):
+    """Gradients of both streams' outputs, fp64, row by row.
+
+    Inputs as for ``swa`` and ``xattn`` (k, v [B, T, Hkv, D]; qx_pre
+    [B, T_out, Hq, D] with row r at position T - T_out + r; qx_pre may have
+    T_out = 0), plus the upstream gradients d_o [B, T, Hq, D] and d_ox
+    [B, T_out, Hq, D] of o and o'. For a row with query q over keys R:
+    p = softmax(K_R q / sqrt(D)), dp = V_R dO, ds = p (dp - p.dp),
+    dq = K_R^T ds / sqrt(D), dK_R += ds q^T / sqrt(D), dV_R += p dO^T
+    (the chain rule through the o_t and o'_t equations of paper text §3.1),
+    then through the scale-offset q = alpha (.) q_pre + beta:
+    dq_pre = alpha (.) dq, d_alpha = sum of dq (.) q_pre, d_beta = sum of dq.
+    Returns a dict of dq_pre, dqx_pre, dk, dv, d_alpha, d_beta, d_alpha_x,
+    d_beta_x (alpha/beta gradients [Hq*D]).
+    """
+    q_pre, qx_pre = _f64(q_pre), _f64(qx_pre)
+    k, v, d_o, d_ox = _f64(k), _f64(v), _f64(d_o), _f64(d_ox)
+    B, T, Hq, D = q_pre.shape
+    Hkv = k.shape[2]
+    T_out = qx_pre.shape[1]
+    T_in = T - T_out
+    kv_of = (np.arange(Hq) // (Hq // Hkv) if head_map is None
+             else np.asarray(head_map, dtype=np.int64))
+    scale = 1.0 / np.sqrt(D)
+    g = {"dq_pre": np.zeros_like(q_pre), "dqx_pre": np.zeros_like(qx_pre),
+         "dk": np.zeros_like(k), "dv": np.zeros_like(v)}
+    for name in ("d_alpha", "d_beta", "d_alpha_x", "d_beta_x"):
+        g[name] = np.zeros((Hq, D))
+
+    def row(b, h, qp, a, be, lo, hi, dO):
+        gkv = kv_of[h]
+        q = a * qp + be
+        K, V = k[b, lo:hi + 1, gkv], v[b, lo:hi + 1, gkv]
+        s = K @ q * scale
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        dp = V @ dO
+        ds = p * (dp - p @ dp)
+        dq = K.T @ ds * scale
+        g["dk"][b, lo:hi + 1, gkv] += np.outer(ds, q) * scale
+        g["dv"][b, lo:hi + 1, gkv] += np.outer(p, dO)
+        return dq
+
+    a2 = _f64(alpha).reshape(Hq, D)
+    b2 = _f64(beta).reshape(Hq, D)
+    ax2 = _f64(alpha_x).reshape(Hq, D)
+    bx2 = _f64(beta_x).reshape(Hq, D)
+    for b in range(B):
+        for h in range(Hq):
+            for t in range(T):
+                dq = row(b, h, q_pre[b, t, h], a2[h], b2[h],
+                         max(0, t - W + 1), t, d_o[b, t, h])
+                g["dq_pre"][b, t, h] = a2[h] * dq
+                g["d_alpha"][h] += dq * q_pre[b, t, h]
+                g["d_beta"][h] += dq
+            for r in range(T_out):
+                dq = row(b, h, qx_pre[b, r, h], ax2[h], bx2[h], 0, T_in + r,
+                         d_ox[b, r, h])
+                g["dqx_pre"][b, r, h] = ax2[h] * dq
+                g["d_alpha_x"][h] += dq * qx_pre[b, r, h]
+                g["d_beta_x"][h] += dq
+    for name in ("d_alpha", "d_beta", "d_alpha_x", "d_beta_x"):
+        g[name] = g[name].reshape(-1)
+    return g

@@ -488,3 +488,98 @@ def test_layer_output_row_order_and_causality():
     expect = [T - 1 <= i < T or i == T + T_out - 1
               for i in range(T + T_out)]
     assert changed.tolist() == expect, (changed, T_in)
+
+
+# --- training gradients (oracle.attn_backward) --------------------------------
+
+def torch_streams_grad(q_pre, qx_pre, a, b, ax, bx, k, v, d_o, d_ox, W,
+                       head_map=None):
+    """torch autograd (fp64) of <o, d_o> + <o', d_ox> through the affine and
+    scaled_dot_product_attention with triangular masks."""
+    t = lambda z: torch.from_numpy(np.ascontiguousarray(z)).double().requires_grad_()  # noqa
+    qp, qxp, A, Bt, AX, BX, K, V = (t(z) for z in
+                                    (q_pre, qx_pre, a, b, ax, bx, k, v))
+    B, T, Hq, D = q_pre.shape
+    T_out = qx_pre.shape[1]
+    Hkv = k.shape[2]
+    idx = (torch.arange(Hq) // (Hq // Hkv) if head_map is None
+           else torch.as_tensor(head_map, dtype=torch.long))
+    Kh = K.index_select(2, idx).permute(0, 2, 1, 3)
+    Vh = V.index_select(2, idx).permute(0, 2, 1, 3)
+    q = (A.reshape(Hq, D) * qp + Bt.reshape(Hq, D)).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(q, Kh, Vh, attn_mask=torch.from_numpy(
+        band_mask(T, W)))
+    loss = (o.permute(0, 2, 1, 3) * torch.from_numpy(d_o)).sum()
+    if T_out:
+        qx = (AX.reshape(Hq, D) * qxp + BX.reshape(Hq, D)).permute(0, 2, 1, 3)
+        ox = F.scaled_dot_product_attention(qx, Kh, Vh, attn_mask=torch.from_numpy(
+            band_mask(T, T, q_offset=T - T_out)))
+        loss = loss + (ox.permute(0, 2, 1, 3) * torch.from_numpy(d_ox)).sum()
+    loss.backward()
+    grad = lambda z: np.zeros(z.shape) if z.grad is None else z.grad.numpy()  # noqa
+    return {"dq_pre": grad(qp), "dqx_pre": grad(qxp), "dk": grad(K),
+            "dv": grad(V), "d_alpha": grad(A), "d_beta": grad(Bt),
+            "d_alpha_x": grad(AX), "d_beta_x": grad(BX)}
+
+
+def grad_case(B, T, T_out, Hq, Hkv, D, seed):
+    q, qx = rnd((B, T, Hq, D), seed), rnd((B, T_out, Hq, D), seed + 1)
+    k, v = rnd((B, T, Hkv, D), seed + 2), rnd((B, T, Hkv, D), seed + 3)
+    a, b = 1 + 0.1 * rnd(Hq * D, seed + 4), 0.1 * rnd(Hq * D, seed + 5)
+    ax, bx = 1 + 0.1 * rnd(Hq * D, seed + 6), 0.1 * rnd(Hq * D, seed + 7)
+    d_o, d_ox = rnd((B, T, Hq, D), seed + 8), rnd((B, T_out, Hq, D), seed + 9)
+    return q, qx, a, b, ax, bx, k, v, d_o, d_ox
+
+
+@pytest.mark.parametrize("B,T,T_out,Hq,Hkv,D,W", [
+    (2, 23, 5, 4, 2, 8, 6),       # SFT-like: a few output rows
+    (1, 17, 17, 2, 1, 16, 4),     # PT: every position an output row
+    (1, 20, 0, 4, 4, 8, 1),       # base stream only, window of one
+    (1, 12, 2, 2, 2, 8, 50),      # window above T
+])
+def test_backward_equals_autograd(B, T, T_out, Hq, Hkv, D, W):
+    args = grad_case(B, T, T_out, Hq, Hkv, D, 700 + T)
+    got = oracle.attn_backward(*args, W)
+    ref = torch_streams_grad(*args, W)
+    for name in ref:
+        np.testing.assert_allclose(got[name], ref[name], rtol=1e-10,
+                                   atol=1e-11, err_msg=name)
+
+
+def test_backward_custom_head_map_equals_autograd():
+    hm = [1, 0, 1]
+    args = list(grad_case(1, 15, 3, 3, 2, 8, 777))
+    got = oracle.attn_backward(*args, 5, head_map=hm)
+    ref = torch_streams_grad(*args, 5, head_map=hm)
+    for name in ref:
+        np.testing.assert_allclose(got[name], ref[name], rtol=1e-10,
+                                   atol=1e-11, err_msg=name)
+
+
+def test_backward_finite_differences():
+    """Central differences of <o, d_o> + <o', d_ox> through the forward
+    oracle for a few coordinates of every input."""
+    B, T, T_out, Hq, Hkv, D, W = 1, 9, 2, 2, 1, 4, 3
+    q, qx, a, b, ax, bx, k, v, d_o, d_ox = grad_case(B, T, T_out, Hq, Hkv, D,
+                                                     901)
+    g = oracle.attn_backward(q, qx, a, b, ax, bx, k, v, d_o, d_ox, W)
+
+    def loss(q, qx, a, b, ax, bx, k, v):
+        o, _ = oracle.swa(q, a, b, k, v, W)
+        ox, _ = oracle.xattn(qx, ax, bx, k, v, T - T_out)
+        return float((o * d_o).sum() + (ox * d_ox).sum())
+
+    base = [q, qx, a, b, ax, bx, k, v]
+    names = ["dq_pre", "dqx_pre", "d_alpha", "d_beta", "d_alpha_x",
+             "d_beta_x", "dk", "dv"]
+    rng = np.random.default_rng(5)
+    eps = 1e-6
+    for i, name in enumerate(names):
+        for _ in range(3):
+            idx = tuple(int(rng.integers(0, n)) for n in base[i].shape)
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[i][idx] += eps
+            minus[i][idx] -= eps
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(fd - g[name][idx]) < 1e-6, (name, idx, fd, g[name][idx])
