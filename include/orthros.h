@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 3
+#define ORTHROS_ABI_VERSION 4
 
 /* dtype codes */
 #define ORTHROS_F32 0
@@ -273,6 +273,53 @@ int orthros_decode_pair_paged(const void *q_pre, const void *qx_pre,
                               int64_t max_len_after, int W,
                               const int32_t *head_map, int dtype, void *ws,
                               size_t ws_bytes, void *stream);
+
+/*
+ * orthros_attn_backward - gradients of both attention streams (training).
+ *
+ * Pages: paper text §3.1 (the o_t and o'_t equations, the query
+ * scale-offset) and §3.2 (pre-training makes every position an output row,
+ * T_out = T; SFT the response positions), where both streams are trained.
+ * Given the forward inputs, the forward outputs o, o' and the upstream
+ * gradients dO, dO', it returns, by the chain rule through each softmax row
+ * (p = softmax(s), dp_j = dO . v_j, ds_j = p_j (dp_j - dO . o)):
+ *   dq_pre  = alpha  (.) sum_j ds_j k_j / sqrt(D)          (base rows)
+ *   dqx_pre = alpha' (.) ...                                (output rows)
+ *   dk_j = sum over the rows of both streams that see key j of
+ *          ds q / sqrt(D), dv_j = sum of p dO  (q = alpha (.) q_pre + beta)
+ *   d_alpha = sum over rows of dq (.) q_pre, d_beta = sum of dq (per
+ *          channel, over batch and rows), likewise d_alpha_x, d_beta_x.
+ * Output row r sits at position T - T_out + r and sees keys [0, that
+ * position]; base row t sees [max(0, t-W+1), t], as in the forward calls.
+ *
+ *   q_pre, o, d_o       [dev] [B, T, Hq, D] bf16
+ *   qx_pre, o_x, d_ox   [dev] [B, T_out, Hq, D] bf16 (NULL when T_out = 0)
+ *   alpha, beta, alpha_x, beta_x [dev] fp32 [Hq*D]
+ *   k_cache, v_cache    [dev] [B, Hkv, cap, D] bf16, rows 0..T-1 used
+ *   dq_pre, dqx_pre     [dev] shapes of q_pre, qx_pre, written
+ *   dk, dv              [dev] [B, T, Hkv, D] bf16 (projection layout), written
+ *   d_alpha, d_beta, d_alpha_x, d_beta_x [dev] fp32 [Hq*D], written
+ *                       (the _x pair is written with zeros when T_out = 0
+ *                       and the pointers are given)
+ *   ws, ws_bytes        [dev] scratch of orthros_backward_workspace_bytes()
+ * bf16, D = 128, 16-byte aligned tensors, T <= 2^24, and every KV head
+ * with 1..8 query heads; otherwise EUNSUPPORTED. Summation order is fixed,
+ * so results are bit-reproducible. Errors: EINVAL, EUNSUPPORTED,
+ * EWORKSPACE, EHIP.
+ */
+int orthros_attn_backward(
+    const void *q_pre, const void *qx_pre, const float *alpha,
+    const float *beta, const float *alpha_x, const float *beta_x,
+    const void *k_cache, const void *v_cache, const void *o, const void *o_x,
+    const void *d_o, const void *d_ox, void *dq_pre, void *dqx_pre, void *dk,
+    void *dv, float *d_alpha, float *d_beta, float *d_alpha_x,
+    float *d_beta_x, int B, int T, int T_out, int Hq, int Hkv, int D,
+    int64_t cap, int W, const int32_t *head_map, int dtype, void *ws,
+    size_t ws_bytes, void *stream);
+
+/* Scratch bytes orthros_attn_backward needs (0 for invalid sizes). */
+size_t orthros_backward_workspace_bytes(int B, int T, int T_out, int Hq,
+                                        int Hkv, int D);
 
 /*
  * orthros_layer_forward - one Orthros attention layer, projections included.

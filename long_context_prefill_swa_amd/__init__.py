@@ -70,6 +70,10 @@ def lib():
                                             i32, vp, i32, vp, sz, vp]
     L.orthros_layer_forward.argtypes = [vp] * 13 + [i32] * 7 + [i64, i32, vp,
                                                                 sz, vp]
+    L.orthros_attn_backward.argtypes = [vp] * 20 + [i32] * 6 + [i64, i32, vp,
+                                                               i32, vp, sz, vp]
+    L.orthros_backward_workspace_bytes.argtypes = [i32] * 6
+    L.orthros_backward_workspace_bytes.restype = sz
     L.orthros_layer_workspace_bytes.argtypes = [i32] * 7
     L.orthros_layer_workspace_bytes.restype = sz
     L.orthros_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i64]
@@ -300,6 +304,58 @@ def orthros_decode_pair_paged(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
         _dtype_code(q_pre), _dev(ws, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(),
         _stream(stream, q_pre)))
+
+
+def orthros_backward_workspace_bytes(B, T, T_out, Hq, Hkv, D):
+    return int(lib().orthros_backward_workspace_bytes(B, T, T_out, Hq, Hkv, D))
+
+
+def orthros_attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
+                          k_cache, v_cache, o, o_x, d_o, d_ox, W,
+                          head_map=None, out=None, ws=None, stream=None):
+    """Gradients of both streams. q_pre, o, d_o [B, T, Hq, D]; qx_pre, o_x,
+    d_ox [B, T_out, Hq, D] (or None with T_out = 0); caches [B, Hkv, cap, D].
+    Returns a dict: dq_pre, dqx_pre, dk, dv ([B, T, Hkv, D]), d_alpha,
+    d_beta, d_alpha_x, d_beta_x ([Hq*D] fp32). `out` may supply them."""
+    B, T, Hq, D = q_pre.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    T_out = 0 if qx_pre is None else qx_pre.shape[1]
+    if tuple(k_cache.shape) != (B, Hkv, cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, Hkv, cap, D]")
+    for name, t in (("o", o), ("d_o", d_o)):
+        if t.shape != q_pre.shape:
+            raise ValueError(f"{name} must have q_pre's shape")
+    if T_out:
+        for name, t in (("o_x", o_x), ("d_ox", d_ox)):
+            if t.shape != qx_pre.shape:
+                raise ValueError(f"{name} must have qx_pre's shape")
+    dev, bf, f32 = q_pre.device, torch.bfloat16, torch.float32
+    g = dict(out or {})
+    g.setdefault("dq_pre", torch.empty_like(q_pre))
+    g.setdefault("dqx_pre", None if not T_out else torch.empty_like(qx_pre))
+    g.setdefault("dk", torch.empty((B, T, Hkv, D), dtype=bf, device=dev))
+    g.setdefault("dv", torch.empty((B, T, Hkv, D), dtype=bf, device=dev))
+    for name in ("d_alpha", "d_beta", "d_alpha_x", "d_beta_x"):
+        g.setdefault(name, torch.empty(Hq * D, dtype=f32, device=dev))
+    if ws is None:
+        ws = workspace(orthros_backward_workspace_bytes(B, T, T_out, Hq, Hkv, D),
+                       dev)
+    hm, _keep = _map(head_map)
+    _check(lib().orthros_attn_backward(
+        _dev(q_pre, "q_pre", bf), _dev(qx_pre, "qx_pre", bf),
+        _dev(alpha, "alpha", f32), _dev(beta, "beta", f32),
+        _dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32),
+        _dev(k_cache, "k_cache", bf), _dev(v_cache, "v_cache", bf),
+        _dev(o, "o", bf), _dev(o_x, "o_x", bf), _dev(d_o, "d_o", bf),
+        _dev(d_ox, "d_ox", bf), _dev(g["dq_pre"], "dq_pre", bf),
+        _dev(g["dqx_pre"], "dqx_pre", bf), _dev(g["dk"], "dk", bf),
+        _dev(g["dv"], "dv", bf), _dev(g["d_alpha"], "d_alpha", f32),
+        _dev(g["d_beta"], "d_beta", f32), _dev(g["d_alpha_x"], "d_alpha_x", f32),
+        _dev(g["d_beta_x"], "d_beta_x", f32), B, T, T_out, Hq, Hkv, D, cap,
+        int(W), hm, ORTHROS_BF16, _dev(ws, "ws"),
+        0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream, q_pre)))
+    return g
 
 
 def orthros_layer_workspace_bytes(B, T, T_out, d_model, Hq, Hkv, D):

@@ -1,0 +1,606 @@
+// Training backward of Orthros attention on gfx950 MFMA (bf16, D = 128).
+//
+// Pages: "Orthros: Phase-Aware Heterogeneous Attention for Efficient
+// Transformers", paper text §3.1 (the o_t and o'_t equations and the query
+// scale-offset) and §3.2 (pre-training duplicates every position as an
+// output row; SFT the response positions), which is where gradients of both
+// streams are needed. The gradients follow the chain rule through one
+// softmax row: with p = softmax(s), s_j = q.k_j / sqrt(D),
+//   dp_j = dO . v_j,  ds_j = p_j (dp_j - dO . o),  dq = sum_j ds_j k_j / sqrt(D),
+//   dk_j += ds_j q / sqrt(D),  dv_j += p_j dO,
+// then dq_pre = alpha (.) dq, d alpha = sum dq (.) q_pre, d beta = sum dq.
+//
+// Three kernels, each in the layouts of v_mfma_f32_16x16x32_bf16 (lane
+// (col = lane % 16, g4 = lane / 16); A rows and B columns on col, the
+// 32-wide contraction split 8 per g4; C holds rows 4 g4 .. 4 g4 + 3 of
+// column col):
+//  * bwd_dq_kernel (per stream): 8 waves, each 32 query rows of one head.
+//    Pass 1 over the band's 64-key tiles forms S^T = K Q^T and the row's
+//    log-sum-exp; pass 2 forms S^T and dP^T = V dO^T again, dS^T, and
+//    dQ^T += K^T dS^T (K^T read with ds_read_b64_tr_b16). It writes
+//    dq_pre, the row's log-sum-exp and dO . o, and per 32-row block the
+//    channel sums that make d alpha and d beta.
+//  * bwd_dkv_kernel (both streams): 4 waves, each 16 keys of one KV head,
+//    over every query head of that KV head and every 32-row block of either
+//    stream that sees the keys: S = Q K^T and dP = dO V^T with K, V held in
+//    registers, then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read
+//    transposed from LDS.
+//  * bwd_reduce_kernel: the per-block channel sums, added in a fixed order.
+// All softmax arithmetic is fp32 in base 2 (log2(e)/sqrt(D) folded into the
+// query operand, as in the forward kernels); P and dS enter the MFMA as bf16.
+#include "common.h"
+
+namespace orthros {
+namespace {
+
+constexpr int D = 128;
+constexpr int kS = D + 16;  // LDS row stride (bf16): 288 bytes
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b,
+                                        const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// 16-byte row chunk `c4` for lane group g4 of row `row` (A/B operand rows).
+__device__ __forceinline__ bf16x8 lds_row8(const uint16_t (*t)[kS], int row,
+                                           int c4, int g4) {
+  return *(const bf16x8 *)&t[row][32 * c4 + 8 * g4];
+}
+
+// Transposed operand (16 channels x 32 rows of the tile, rows in the order
+// the packed C fragments use): rows 4 g4 + (j16 / 4) (+16), channels
+// 16 dt + 4 (j16 % 4).
+__device__ __forceinline__ bf16x8 lds_tr8(const uint16_t (*t)[kS], int row0,
+                                          int g4, int j16, int dt) {
+  const uint16_t *p = &t[row0 + 4 * g4 + (j16 >> 2)][16 * dt + 4 * (j16 & 3)];
+  const bf16x4 lo4 = lds_read_tr(p);
+  const bf16x4 hi4 = lds_read_tr(p + 16 * kS);
+  return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return bf16_bits_to_f32(w & 0xffffu); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return bf16_bits_to_f32(w >> 16); }
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
+}
+
+// First key of row position p's range (W >= p + 1 means the whole prefix).
+__device__ __forceinline__ int range_lo(int p, int W) {
+  return p >= W ? p - W + 1 : 0;
+}
+
+// ============================================================================
+// dQ (and the row statistics) of one stream
+// ============================================================================
+template <int GS>
+struct DqSmem {
+  uint16_t k[64][kS];
+  uint16_t v[64][kS];
+  float ab[GS][2][D];
+};
+
+template <int GS>
+__global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
+                                                        HeadGroups groups) {
+  constexpr int kRowsWg = 32 * (8 / GS);
+  __shared__ __attribute__((aligned(16))) DqSmem<GS> sm;
+  const int n_wg_rows = (a.nrows + kRowsWg - 1) / kRowsWg;
+  const int wr = blockIdx.x % n_wg_rows;
+  const int rest = blockIdx.x / n_wg_rows;
+  const int gi = rest % groups.n_groups;
+  const int b = rest / groups.n_groups;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g4 = lane >> 4;
+  const int hs = w % GS, rb = w / GS;
+  const int head = groups.q[gi][hs];
+  const int kvh = groups.kv[gi];
+  const float qs = kLog2e * rsqrtf((float)D);
+
+  for (int i = tid; i < GS * 2 * D; i += 512) {
+    const int s = i / (2 * D), which = (i / D) & 1, d = i % D;
+    const int h = max((int)groups.q[gi][s], 0);
+    sm.ab[s][which][d] = (which ? a.beta : a.alpha)[h * D + d] * qs;
+  }
+
+  // rows of this wave: r0 + 16 h2 + col (h2 = 0, 1)
+  const int r_wg = wr * kRowsWg;
+  const int r0 = r_wg + 32 * rb;
+  const int p_wg_first = a.q_offset + r_wg;
+  const int p_wg_last = a.q_offset + min(r_wg + kRowsWg, a.nrows) - 1;
+  const int lo_wg = range_lo(p_wg_first, a.W);
+  const int hi_wg = min(p_wg_last, a.n_keys - 1);
+  const int kt_lo = lo_wg / 64, kt_hi = hi_wg / 64;
+  const bool wave_on = head >= 0 && r0 < a.nrows;
+  const int p_w_first = a.q_offset + r0;
+  const int p_w_last = a.q_offset + min(r0 + 32, a.nrows) - 1;
+  const int lo_w = range_lo(p_w_first, a.W);
+
+  // per-lane row operands (rows past the end re-read the last row)
+  const int hq = max(head, 0);
+  int prow[2];
+  bool row_ok[2];
+  bf16x8 qop[2][4], doop[2][4];
+  float delta[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int r = r0 + 16 * h2 + col;
+    row_ok[h2] = wave_on && r < a.nrows;
+    prow[h2] = a.q_offset + r;
+    const int rc = min(r, a.nrows - 1);
+    const int64_t off = (((int64_t)b * a.nrows + rc) * a.Hq + hq) * D;
+    float dsum = 0.0f;  // dO . o over this lane's 32 channels
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int d0 = 32 * c4 + 8 * g4;
+      const uint4 oraw = *(const uint4 *)(a.o + off + d0);
+      const uint4 graw = *(const uint4 *)(a.d_o + off + d0);
+      doop[h2][c4] = as_bf16x8(graw);
+      const uint32_t ow[4] = {oraw.x, oraw.y, oraw.z, oraw.w};
+      const uint32_t gw[4] = {graw.x, graw.y, graw.z, graw.w};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        dsum += bf16_lo(gw[e2]) * bf16_lo(ow[e2]) + bf16_hi(gw[e2]) * bf16_hi(ow[e2]);
+    }
+    dsum += __shfl_xor(dsum, 16, 64);
+    dsum += __shfl_xor(dsum, 32, 64);
+    delta[h2] = dsum;
+  }
+
+  // K/V tile staging: 2 x 16 bytes of K and of V per thread
+  const int64_t slab = ((int64_t)b * a.n_kv + kvh) * a.cap * D;
+  const uint32_t slab_bytes = (uint32_t)a.n_keys * (D * 2);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.k_cache + slab), 0, slab_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.v_cache + slab), 0, slab_bytes, kBufferWord3);
+  uint4 kst[2], vst[2];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = (uint32_t)kt * (64 * D * 2) + 16u * (uint32_t)(tid + 512 * i);
+      kst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      vst[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 512 * i;
+      *(uint4 *)&sm.k[idx >> 4][8 * (idx & 15)] = kst[i];
+      *(uint4 *)&sm.v[idx >> 4][8 * (idx & 15)] = vst[i];
+    }
+  };
+  load(kt_lo);
+  __syncthreads();  // alpha/beta table
+
+  // query operand: bf16(alpha' q + beta') with the base-2 scale folded in
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int rc = min(r0 + 16 * h2 + col, a.nrows - 1);
+    const int64_t off = (((int64_t)b * a.nrows + rc) * a.Hq + hq) * D;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const int d0 = 32 * c4 + 8 * g4;
+      const uint4 qraw = *(const uint4 *)(a.q + off + d0);
+      const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = (e & 1) ? bf16_hi(qw[e >> 1]) : bf16_lo(qw[e >> 1]);
+        qop[h2][c4][e] = (__bf16)(sm.ab[hs][0][d0 + e] * qv + sm.ab[hs][1][d0 + e]);
+      }
+    }
+  }
+
+  // S^T block (16 keys of sub-block kb x 16 rows of half h2), masked
+  auto scores = [&](int kt, int kb, int h2) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+      s = mfma16(lds_row8(sm.k, 16 * kb + col, c4, g4), qop[h2][c4], s);
+    // key kept iff lo <= key <= p, i.e. (unsigned)(key - lo) <= p - lo
+    const int lo = range_lo(prow[h2], a.W);
+    const uint32_t u0 = (uint32_t)(kt * 64 + 16 * kb + 4 * g4 - lo);
+    const uint32_t span = (uint32_t)(prow[h2] - lo);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      s[i] = (u0 + i <= span) ? s[i] : -INFINITY;
+    return s;
+  };
+
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+  float lse[2] = {0.0f, 0.0f};
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[h2][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int j16 = col;
+
+  const int n_tiles = kt_hi - kt_lo + 1;
+  auto next_tile = [&](int kt) {
+    __syncthreads();  // the previous tile's readers are done
+    store();
+    __syncthreads();
+    (void)kt;
+  };
+  auto wave_needs = [&](int kt) {
+    const int k_first = kt * 64, k_last = k_first + 63;
+    return wave_on && k_last >= lo_w && k_first <= p_w_last;
+  };
+
+  // ---- pass 1: row maxima and sums ----------------------------------------
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    next_tile(kt);
+    load(kt < kt_hi ? kt + 1 : kt_lo);  // pass 2 starts over at kt_lo
+    if (!wave_needs(kt)) continue;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x4 s[4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = scores(kt, kb, h2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kb][i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m[h2], tmax);
+      const float ms = (mn == -INFINITY) ? 0.0f : mn;
+      float ps = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ps += __builtin_amdgcn_exp2f(s[kb][i] - ms);
+      l[h2] = l[h2] * __builtin_amdgcn_exp2f(m[h2] - ms) + ps;
+      m[h2] = mn;
+    }
+  }
+  // row log-sum-exp (base 2) over the four lane groups
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    float lt = l[h2];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    lse[h2] = m[h2] + __log2f(lt);
+  }
+
+  // ---- pass 2: dS^T and dQ^T ------------------------------------------------
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    next_tile(kt);
+    if (kt < kt_hi) load(kt + 1);
+    if (!wave_needs(kt)) continue;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp) {
+        bf16x8 dsop;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kb = 2 * kp + half;
+          const f32x4 s = scores(kt, kb, h2);
+          f32x4 dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4)
+            dp = mfma16(lds_row8(sm.v, 16 * kb + col, c4, g4), doop[h2][c4], dp);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // masked keys (and rows with no key at all) give p = 0
+            const float p = s[i] == -INFINITY
+                                ? 0.0f
+                                : __builtin_amdgcn_exp2f(s[i] - lse[h2]);
+            dsop[4 * half + i] = (__bf16)(p * (dp[i] - delta[h2]));
+          }
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          acc[h2][dt] = mfma16(lds_tr8(sm.k, 32 * kp, g4, j16, dt), dsop, acc[h2][dt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // ---- outputs ---------------------------------------------------------------
+  if (!wave_on) return;
+  const float inv_sqrt_d = rsqrtf((float)D);
+  float sa[8][4], sb[8][4];  // channel sums over this wave's rows
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[dt][i] = sb[dt][i] = 0.0f;
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const int r = r0 + 16 * h2 + col;
+    const int rc = min(r, a.nrows - 1);
+    const int64_t off = (((int64_t)b * a.nrows + rc) * a.Hq + hq) * D;
+
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d0 = 16 * dt + 4 * g4;
+      const uint2 qraw = *(const uint2 *)(a.q + off + d0);
+      const float qv[4] = {bf16_lo(qraw.x), bf16_hi(qraw.x), bf16_lo(qraw.y),
+                           bf16_hi(qraw.y)};
+      const float4 al = *(const float4 *)(a.alpha + hq * D + d0);
+      const float alv[4] = {al.x, al.y, al.z, al.w};
+      float g[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float dq = row_ok[h2] ? acc[h2][dt][i] * inv_sqrt_d : 0.0f;
+        g[i] = alv[i] * dq;
+        sa[dt][i] += dq * qv[i];
+        sb[dt][i] += dq;
+      }
+      if (row_ok[h2])
+        *(uint2 *)(a.dq + off + d0) = make_uint2(pack2(g[0], g[1]), pack2(g[2], g[3]));
+    }
+    if (g4 == 0 && row_ok[h2]) {
+      const int64_t si = ((int64_t)b * a.Hq + head) * a.nrows + r;
+      a.lse[si] = lse[h2];
+      a.delta[si] = delta[h2];
+    }
+  }
+  // sum over the 16 rows of a lane group (h2 already folded in)
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        sa[dt][i] += __shfl_xor(sa[dt][i], off, 64);
+        sb[dt][i] += __shfl_xor(sb[dt][i], off, 64);
+      }
+    }
+  if (col == 0) {
+    const int n_rb = (a.nrows + 31) / 32;
+    const int rbg = r0 / 32;
+    float *pa = a.part + ((((int64_t)b * n_rb + rbg) * a.Hq + head) * 2) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d0 = 16 * dt + 4 * g4;
+      *(float4 *)(pa + d0) = make_float4(sa[dt][0], sa[dt][1], sa[dt][2], sa[dt][3]);
+      *(float4 *)(pa + D + d0) = make_float4(sb[dt][0], sb[dt][1], sb[dt][2], sb[dt][3]);
+    }
+  }
+}
+
+// ============================================================================
+// dK, dV of one KV head and 64 keys, over both streams
+// ============================================================================
+struct DkvSmem {
+  uint16_t q[32][kS];
+  uint16_t g[32][kS];
+  float lse[32], delta[32];
+  float ab[kMaxGroupSize][4][D];  // alpha, beta, alpha', beta' per head
+};
+
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdKvArgs a,
+                                                         HeadGroups groups) {
+  __shared__ __attribute__((aligned(16))) DkvSmem sm;
+  const int n_kt = (a.T + 63) / 64;
+  const int kt = blockIdx.x % n_kt;
+  const int rest = blockIdx.x / n_kt;
+  const int gi = rest % groups.n_groups;  // the one group of this KV head
+  const int b = rest / groups.n_groups;
+  const int kvh = groups.kv[gi];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, g4 = lane >> 4, j16 = col;
+  const int k0 = kt * 64;
+  const int key = k0 + 16 * w + col;  // this lane's key (B columns)
+  const float qs = kLog2e * rsqrtf((float)D);
+
+  // K and V rows of this wave's keys as B operands (channels 32 c4 + 8 g4)
+  bf16x8 kop[4], vop[4];
+  {
+    const int kc = min(key, a.T - 1);
+    const int64_t off = (((int64_t)b * a.n_kv + kvh) * a.cap + kc) * D;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      kop[c4] = as_bf16x8(*(const uint4 *)(a.k_cache + off + 32 * c4 + 8 * g4));
+      vop[c4] = as_bf16x8(*(const uint4 *)(a.v_cache + off + 32 * c4 + 8 * g4));
+    }
+  }
+  f32x4 dk[8], dv[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Work list: (query head of this KV head) x (stream) x (32-row block).
+  const int T_in = a.T - a.T_out;
+  const int base_lo = (int)(k0 / 32);
+  const int base_hi = min(a.T - 1, k0 + 63 + a.W - 1) / 32;  // W <= T
+  const int n_base = base_hi - base_lo + 1;
+  int out_lo = 0, n_out = 0;
+  if (a.T_out > 0) {
+    out_lo = max(0, k0 - T_in) / 32;
+    n_out = (a.T_out - 1) / 32 - out_lo + 1;
+    if (n_out < 0) n_out = 0;
+  }
+  const int per_head = n_base + n_out;
+
+  // query heads of this KV head: the group's slots up to the first empty one
+  int n_heads = 0;
+  while (n_heads < groups.gsize && groups.q[gi][n_heads] >= 0) ++n_heads;
+  const int n_it = n_heads * per_head;
+
+  // alpha, beta of both streams for the group's heads, base-2 scale folded
+  for (int i = tid; i < n_heads * 4 * D; i += 256) {
+    const int hi = i / (4 * D), which = (i / D) % 4, d = i % D;
+    const float *src = which == 0 ? a.alpha : which == 1 ? a.beta
+                     : which == 2 ? a.alpha_x : a.beta_x;
+    sm.ab[hi][which][d] = src[groups.q[gi][hi] * D + d] * qs;
+  }
+
+  struct Item { int hi, s, qb; };
+  auto decode = [&](int it) {
+    const int hi = it / per_head, rr = it % per_head;
+    const int s = rr >= n_base;
+    return Item{hi, s, s ? out_lo + (rr - n_base) : base_lo + rr};
+  };
+
+  // staging: thread -> rows (tid / 16) and (tid / 16 + 16), one 16-byte
+  // chunk (8 channels) of each of Q and dO
+  const int srow = tid >> 4, sd0 = 8 * (tid & 15);
+  uint4 q0, q1, g0, g1;
+  float st_lse = 0.0f, st_delta = 0.0f;
+  auto load = [&](int it) {
+    const Item itm = decode(it);
+    const int h = groups.q[gi][itm.hi];
+    const int nrows = itm.s ? a.T_out : a.T;
+    const uint16_t *qsrc = itm.s ? a.qx : a.q;
+    const uint16_t *gsrc = itm.s ? a.d_ox : a.d_o;
+    const int ra = min(itm.qb * 32 + srow, nrows - 1);
+    const int rb2 = min(itm.qb * 32 + srow + 16, nrows - 1);
+    const int64_t oa = (((int64_t)b * nrows + ra) * a.Hq + h) * D + sd0;
+    const int64_t ob = (((int64_t)b * nrows + rb2) * a.Hq + h) * D + sd0;
+    q0 = *(const uint4 *)(qsrc + oa);
+    g0 = *(const uint4 *)(gsrc + oa);
+    q1 = *(const uint4 *)(qsrc + ob);
+    g1 = *(const uint4 *)(gsrc + ob);
+    if (tid < 32) {
+      const int r = min(itm.qb * 32 + tid, nrows - 1);
+      const int64_t si = ((int64_t)b * a.Hq + h) * nrows + r;
+      st_lse = (itm.s ? a.lse_x : a.lse)[si];
+      st_delta = (itm.s ? a.delta_x : a.delta)[si];
+    }
+  };
+  auto qrow = [&](uint4 raw, const float *al, const float *be) {
+    const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o4[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      const int d = sd0 + 2 * e2;
+      o4[e2] = pack2(al[d] * bf16_lo(qw[e2]) + be[d],
+                     al[d + 1] * bf16_hi(qw[e2]) + be[d + 1]);
+    }
+    return make_uint4(o4[0], o4[1], o4[2], o4[3]);
+  };
+  auto store = [&](int it) {
+    const Item itm = decode(it);
+    const float *al = sm.ab[itm.hi][2 * itm.s];
+    const float *be = sm.ab[itm.hi][2 * itm.s + 1];
+    *(uint4 *)&sm.q[srow][sd0] = qrow(q0, al, be);
+    *(uint4 *)&sm.q[srow + 16][sd0] = qrow(q1, al, be);
+    *(uint4 *)&sm.g[srow][sd0] = g0;
+    *(uint4 *)&sm.g[srow + 16][sd0] = g1;
+    if (tid < 32) {
+      sm.lse[tid] = st_lse;
+      sm.delta[tid] = st_delta;
+    }
+  };
+
+  if (n_it > 0) load(0);
+  for (int it = 0; it < n_it; ++it) {
+    __syncthreads();
+    store(it);
+    __syncthreads();
+    if (it + 1 < n_it) load(it + 1);
+    const Item itm = decode(it);
+    const int hi = itm.hi, s = itm.s, qb = itm.qb;
+    const int nrows = s ? a.T_out : a.T;
+    const int pos0 = (s ? T_in : 0) + qb * 32;  // position of row 0
+    const int Ws = s ? a.T : a.W;
+    bf16x8 pop, dsop;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        sc = mfma16(lds_row8(sm.q, 16 * h2 + col, c4, g4), kop[c4], sc);
+        dp = mfma16(lds_row8(sm.g, 16 * h2 + col, c4, g4), vop[c4], dp);
+      }
+      // C rows are query rows 16 h2 + 4 g4 + i, the column is this key
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 16 * h2 + 4 * g4 + i;
+        const int p = pos0 + rl;
+        const bool ok = qb * 32 + rl < nrows && key < a.T && key <= p &&
+                        key >= range_lo(p, Ws);
+        const float pr = ok ? __builtin_amdgcn_exp2f(sc[i] - sm.lse[rl]) : 0.0f;
+        pop[4 * h2 + i] = (__bf16)pr;
+        dsop[4 * h2 + i] = (__bf16)(pr * (dp[i] - sm.delta[rl]));
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      dv[dt] = mfma16(lds_tr8(sm.g, 0, g4, j16, dt), pop, dv[dt]);
+      dk[dt] = mfma16(lds_tr8(sm.q, 0, g4, j16, dt), dsop, dk[dt]);
+    }
+  }
+
+  // dK = dS^T (c q) / (c sqrt(D)) with c sqrt(D) = log2(e); dV = P^T dO
+  if (key >= a.T) return;
+  const float kscale = 1.0f / kLog2e;
+  const int64_t off = (((int64_t)b * a.T + key) * a.n_kv + kvh) * D;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int d0 = 16 * dt + 4 * g4;
+    *(uint2 *)(a.dk + off + d0) =
+        make_uint2(pack2(dk[dt][0] * kscale, dk[dt][1] * kscale),
+                   pack2(dk[dt][2] * kscale, dk[dt][3] * kscale));
+    *(uint2 *)(a.dv + off + d0) =
+        make_uint2(pack2(dv[dt][0], dv[dt][1]), pack2(dv[dt][2], dv[dt][3]));
+  }
+}
+
+// d alpha, d beta [Hq*D] from the per-block sums [B, n_rb, Hq, 2, D].
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(
+    const float *__restrict__ part, float *__restrict__ d_alpha,
+    float *__restrict__ d_beta, int B, int n_rb, int Hq) {
+  const int h = blockIdx.x, which = threadIdx.x / D, d = threadIdx.x % D;
+  float s = 0.0f;
+  for (int b = 0; b < B; ++b)
+    for (int r = 0; r < n_rb; ++r)
+      s += part[((((int64_t)b * n_rb + r) * Hq + h) * 2 + which) * D + d];
+  (which ? d_beta : d_alpha)[h * D + d] = s;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq(const BwdStreamArgs &a, const HeadGroups &groups,
+                         int B, hipStream_t stream) {
+  const int rows_wg = 32 * (8 / groups.gsize);
+  const int n_wg_rows = (a.nrows + rows_wg - 1) / rows_wg;
+  const dim3 grid((unsigned)(n_wg_rows * groups.n_groups * B));
+  switch (groups.gsize) {
+    case 1: hipLaunchKernelGGL(bwd_dq_kernel<1>, grid, dim3(512), 0, stream, a, groups); break;
+    case 2: hipLaunchKernelGGL(bwd_dq_kernel<2>, grid, dim3(512), 0, stream, a, groups); break;
+    case 4: hipLaunchKernelGGL(bwd_dq_kernel<4>, grid, dim3(512), 0, stream, a, groups); break;
+    case 8: hipLaunchKernelGGL(bwd_dq_kernel<8>, grid, dim3(512), 0, stream, a, groups); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const BwdKvArgs &a, const HeadGroups &groups,
+                          int B, hipStream_t stream) {
+  const int n_kt = (a.T + 63) / 64;
+  hipLaunchKernelGGL(bwd_dkv_kernel,
+                     dim3((unsigned)(n_kt * groups.n_groups * B)), dim3(256), 0,
+                     stream, a, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const float *part, float *d_alpha, float *d_beta,
+                             int B, int n_rb, int Hq, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(Hq), dim3(2 * D), 0, stream, part,
+                     d_alpha, d_beta, B, n_rb, Hq);
+  return hipGetLastError();
+}
+
+}  // namespace orthros

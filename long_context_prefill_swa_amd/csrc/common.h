@@ -97,6 +97,34 @@ hipError_t launch_band_mfma(const void *q, const float *alpha,
                             const HeadGroups &groups, int n_kv,
                             hipStream_t stream);
 
+// ---- training backward (bf16, D = 128) -------------------------------------
+// One stream's rows: positions q_offset + r, keys [max(0, p-W+1), p].
+struct BwdStreamArgs {
+  const uint16_t *q, *o, *d_o;          // [B, nrows, Hq, D]
+  const uint16_t *k_cache, *v_cache;    // [B, n_kv, cap, D]
+  const float *alpha, *beta;            // [Hq*D]
+  uint16_t *dq;                         // [B, nrows, Hq, D] d q_pre
+  float *lse, *delta;                   // [B, Hq, nrows] base-2 lse, dO . o
+  float *part;                          // [B, ceil(nrows/32), Hq, 2, D]
+  int nrows, Hq, n_kv, n_keys, W, q_offset;  // W <= n_keys
+  int64_t cap;
+};
+// Both streams, for dK and dV [B, T, n_kv, D].
+struct BwdKvArgs {
+  const uint16_t *q, *qx, *d_o, *d_ox, *k_cache, *v_cache;
+  const float *alpha, *beta, *alpha_x, *beta_x;
+  const float *lse, *delta, *lse_x, *delta_x;
+  uint16_t *dk, *dv;
+  int T, T_out, Hq, n_kv, W;  // W <= T
+  int64_t cap;
+};
+hipError_t launch_bwd_dq(const BwdStreamArgs &a, const HeadGroups &groups,
+                         int B, hipStream_t stream);
+hipError_t launch_bwd_dkv(const BwdKvArgs &a, const HeadGroups &groups,
+                          int B, hipStream_t stream);
+hipError_t launch_bwd_reduce(const float *part, float *d_alpha, float *d_beta,
+                             int B, int n_rb, int Hq, hipStream_t stream);
+
 // Rolling-window attention for small windows, bf16, D = 128, 4 query heads
 // per KV head, rows at positions 0 .. nrows-1, 1 <= W <= kRollMaxWindow.
 constexpr int kRollMaxWindow = 129;

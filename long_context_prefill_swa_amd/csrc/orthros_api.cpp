@@ -604,3 +604,173 @@ int orthros_check_device_errors(void *stream) {
 }
 
 }  // extern "C"
+
+// ---- training backward -------------------------------------------------------
+
+namespace {
+
+struct BwdWs {
+  size_t lse, delta, lse_x, delta_x, part, part_x, total;
+};
+
+size_t al256(size_t n) { return (n + 255) & ~size_t(255); }
+
+BwdWs bwd_ws(int B, int T, int T_out, int Hq, int D) {
+  BwdWs w;
+  size_t off = 0;
+  const size_t rows = (size_t)B * Hq * 4;
+  w.lse = off;
+  off += al256(rows * T);
+  w.delta = off;
+  off += al256(rows * T);
+  w.lse_x = off;
+  off += al256(rows * T_out);
+  w.delta_x = off;
+  off += al256(rows * T_out);
+  w.part = off;
+  off += al256((size_t)B * ((T + 31) / 32) * Hq * 2 * D * 4);
+  w.part_x = off;
+  off += al256((size_t)B * ((T_out + 31) / 32) * Hq * 2 * D * 4);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+size_t orthros_backward_workspace_bytes(int B, int T, int T_out, int Hq,
+                                        int Hkv, int D) {
+  if (B < 1 || T < 1 || T_out < 0 || T_out > T || Hq < 1 || Hkv < 1 ||
+      Hq > ORTHROS_MAX_HEADS || Hkv > ORTHROS_MAX_HEADS || D < 1 ||
+      D > ORTHROS_MAX_D)
+    return 0;
+  return bwd_ws(B, T, T_out, Hq, D).total;
+}
+
+int orthros_attn_backward(
+    const void *q_pre, const void *qx_pre, const float *alpha,
+    const float *beta, const float *alpha_x, const float *beta_x,
+    const void *k_cache, const void *v_cache, const void *o, const void *o_x,
+    const void *d_o, const void *d_ox, void *dq_pre, void *dqx_pre, void *dk,
+    void *dv, float *d_alpha, float *d_beta, float *d_alpha_x,
+    float *d_beta_x, int B, int T, int T_out, int Hq, int Hkv, int D,
+    int64_t cap, int W, const int32_t *head_map, int dtype, void *ws,
+    size_t ws_bytes, void *stream) {
+  clear_error();
+  int rc = check_dtype_d(dtype, D);
+  if (rc) return rc;
+  if (dtype != ORTHROS_BF16 || D != 128)
+    return fail(ORTHROS_EUNSUPPORTED, "the backward needs bf16 and D = 128 (D=%d)", D);
+  if ((rc = check_heads(Hq, Hkv))) return rc;
+  if (B < 0 || T < 0 || T_out < 0)
+    return fail(ORTHROS_EINVAL, "negative size (B=%d, T=%d, T_out=%d)", B, T, T_out);
+  if (T_out > T) return fail(ORTHROS_EINVAL, "T_out=%d exceeds T=%d", T_out, T);
+  if (W < 1) return fail(ORTHROS_EINVAL, "window W=%d must be >= 1", W);
+  if (cap < T || cap > INT32_MAX)
+    return fail(ORTHROS_EINVAL, "cap=%lld must hold the T=%d rows", (long long)cap, T);
+  HeadMap map;
+  HeadGroups groups;
+  if ((rc = build_maps(head_map, Hq, Hkv, &map, &groups))) return rc;
+  {
+    int seen[kMaxHeads] = {0};
+    for (int g = 0; g < groups.n_groups; ++g) ++seen[groups.kv[g]];
+    for (int g = 0; g < Hkv; ++g)
+      if (seen[g] != 1)
+        return fail(ORTHROS_EUNSUPPORTED,
+                    "the backward needs 1..%d query heads on every KV head "
+                    "(KV head %d has %s)", kMaxGroupSize, g,
+                    seen[g] ? "more" : "none");
+  }
+  if (B == 0 || T == 0) return ORTHROS_OK;
+  if (!q_pre || !alpha || !beta || !k_cache || !v_cache || !o || !d_o ||
+      !dq_pre || !dk || !dv || !d_alpha || !d_beta)
+    return fail(ORTHROS_EINVAL, "null pointer argument");
+  if (T_out > 0 && (!qx_pre || !alpha_x || !beta_x || !o_x || !d_ox || !dqx_pre ||
+                    !d_alpha_x || !d_beta_x))
+    return fail(ORTHROS_EINVAL, "null pointer argument (output stream)");
+  int64_t n_elems;
+  if (!tensor_elems(&n_elems, {B, Hkv, cap, D, 2}) ||
+      !tensor_elems(&n_elems, {B, T, Hq, D, 2}))
+    return fail(ORTHROS_EINVAL, "tensor size overflows");
+  if (!mfma_eligible(dtype, D, T, {q_pre, k_cache, v_cache, o, d_o, dq_pre, dk, dv,
+                                   alpha, beta, d_alpha, d_beta}) ||
+      (T_out > 0 && !mfma_eligible(dtype, D, T, {qx_pre, o_x, d_ox, dqx_pre,
+                                                 alpha_x, beta_x})))
+    return fail(ORTHROS_EUNSUPPORTED,
+                "the backward needs 16-byte aligned tensors and T <= 2^24");
+  const BwdWs w = bwd_ws(B, T, T_out, Hq, D);
+  if (!ws || ws_bytes < w.total)
+    return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+  char *base = static_cast<char *>(ws);
+  const int Wb = W < T ? W : T;
+  const hipStream_t st = as_stream(stream);
+
+  BwdStreamArgs sa;
+  sa.q = (const uint16_t *)q_pre;
+  sa.o = (const uint16_t *)o;
+  sa.d_o = (const uint16_t *)d_o;
+  sa.k_cache = (const uint16_t *)k_cache;
+  sa.v_cache = (const uint16_t *)v_cache;
+  sa.alpha = alpha;
+  sa.beta = beta;
+  sa.dq = (uint16_t *)dq_pre;
+  sa.lse = (float *)(base + w.lse);
+  sa.delta = (float *)(base + w.delta);
+  sa.part = (float *)(base + w.part);
+  sa.nrows = T;
+  sa.Hq = Hq;
+  sa.n_kv = Hkv;
+  sa.n_keys = T;
+  sa.W = Wb;
+  sa.q_offset = 0;
+  sa.cap = cap;
+  hipError_t e = launch_bwd_dq(sa, groups, B, st);
+  if (e != hipSuccess) return hip_fail("backward dq launch", e);
+  if (T_out > 0) {
+    BwdStreamArgs sx = sa;
+    sx.q = (const uint16_t *)qx_pre;
+    sx.o = (const uint16_t *)o_x;
+    sx.d_o = (const uint16_t *)d_ox;
+    sx.alpha = alpha_x;
+    sx.beta = beta_x;
+    sx.dq = (uint16_t *)dqx_pre;
+    sx.lse = (float *)(base + w.lse_x);
+    sx.delta = (float *)(base + w.delta_x);
+    sx.part = (float *)(base + w.part_x);
+    sx.nrows = T_out;
+    sx.W = T;
+    sx.q_offset = T - T_out;
+    e = launch_bwd_dq(sx, groups, B, st);
+    if (e != hipSuccess) return hip_fail("backward dq launch (output stream)", e);
+  }
+  BwdKvArgs ka;
+  ka.q = (const uint16_t *)q_pre;
+  ka.qx = (const uint16_t *)qx_pre;
+  ka.d_o = (const uint16_t *)d_o;
+  ka.d_ox = (const uint16_t *)d_ox;
+  ka.k_cache = (const uint16_t *)k_cache;
+  ka.v_cache = (const uint16_t *)v_cache;
+  ka.alpha = alpha;
+  ka.beta = beta;
+  ka.alpha_x = alpha_x;
+  ka.beta_x = beta_x;
+  ka.lse = sa.lse;
+  ka.delta = sa.delta;
+  ka.lse_x = (float *)(base + w.lse_x);
+  ka.delta_x = (float *)(base + w.delta_x);
+  ka.dk = (uint16_t *)dk;
+  ka.dv = (uint16_t *)dv;
+  ka.T = T;
+  ka.T_out = T_out;
+  ka.Hq = Hq;
+  ka.n_kv = Hkv;
+  ka.W = Wb;
+  ka.cap = cap;
+  e = launch_bwd_dkv(ka, groups, B, st);
+  if (e != hipSuccess) return hip_fail("backward dk/dv launch", e);
+  e = launch_bwd_reduce(sa.part, d_alpha, d_beta, B, (T + 31) / 32, Hq, st);
+  if (e == hipSuccess && d_alpha_x && d_beta_x)
+    e = launch_bwd_reduce((float *)(base + w.part_x), d_alpha_x, d_beta_x, B,
+                          (T_out + 31) / 32, Hq, st);
+  if (e != hipSuccess) return hip_fail("backward reduce launch", e);
+  return ORTHROS_OK;
+}

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.orthros_abi_version() == 3
+    assert L.orthros_abi_version() == 4
     for code in (OK, EINVAL, EUNSUP, ECAP, EWS, EHIP):
         assert L.orthros_strerror(code)
     assert b"unknown" in L.orthros_strerror(42)
@@ -276,3 +276,36 @@ def test_layer_workspace_covers_the_intermediates(L):
     assert need >= inter + (64 << 20)
     assert L.orthros_layer_workspace_bytes(1, 10, 11, 512, Hq, Hkv, D) == 0
     assert layer(L, B=0) == OK
+
+
+def bwd(L, ws_bytes=None, **kw):
+    a = dict(B=1, T=64, T_out=2, Hq=4, Hkv=2, D=128, cap=64, W=16, hmap=None,
+             dtype=BF16, q=FAKE)
+    a.update(kw)
+    need = L.orthros_backward_workspace_bytes(a["B"], a["T"], a["T_out"],
+                                              a["Hq"], a["Hkv"], a["D"])
+    return L.orthros_attn_backward(
+        a["q"], *([FAKE] * 19), a["B"], a["T"], a["T_out"], a["Hq"],
+        a["Hkv"], a["D"], a["cap"], a["W"], a["hmap"], a["dtype"], FAKE,
+        need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=F32), EUNSUP, "bf16"),
+    (dict(D=64), EUNSUP, "D = 128"),
+    (dict(T_out=65), EINVAL, "T_out"),
+    (dict(W=0), EINVAL, "window"),
+    (dict(cap=63), EINVAL, "cap"),
+    (dict(Hq=32, Hkv=2), EUNSUP, "query heads"),
+    (dict(q=None), EINVAL, "null"),
+    (dict(ws_bytes=100), EWS, "workspace"),
+])
+def test_attn_backward_rejects(L, kw, code, needle):
+    assert bwd(L, **kw) == code
+    assert needle in last(L)
+
+
+def test_attn_backward_kv_head_without_queries_rejected(L):
+    p, keep = hmap([0, 0, 0, 0])       # KV head 1 has no query head
+    assert bwd(L, hmap=p) == EUNSUP and "none" in last(L)
+    assert bwd(L, B=0) == OK

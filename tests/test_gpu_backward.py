@@ -1,0 +1,97 @@
+"""GPU parity of the training backward (both streams) against the fp64
+oracle's attn_backward, through the C ABI.
+
+Inputs are seeded N(0, 1) draws rounded to bf16; the forward outputs o, o'
+come from the library's own forward calls (the backward takes them as
+inputs, as a training step would), and the oracle gets the exact bf16 bits
+of every input. Tolerances: the bf16 gate (max-abs 2e-2, rel-L2 1e-2) is
+stated for unit-scale values; gradients are not unit-scale (dK, dV and the
+scale-offset gradients are sums over many rows, and a bf16 result of
+magnitude 4 is itself only good to 2^-7), so every gradient's max-abs gate
+is 2e-2 times max(1, its largest reference magnitude), with rel-L2 1e-2
+unchanged."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_prefill_swa_amd as lo
+import oracle
+from gpu_util import TOL, compare, f64, make_cache, say
+from workloads import normal
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF = torch.bfloat16
+
+
+def case(B, T, T_out, Hq, Hkv, W, seed, head_map=None):
+    D = 128
+    q = normal((B, T, Hq, D), seed, BF, DEV)
+    qx = normal((B, T_out, Hq, D), seed + 1, BF, DEV) if T_out else None
+    k = normal((B, T, Hkv, D), seed + 2, BF, DEV)
+    v = normal((B, T, Hkv, D), seed + 3, BF, DEV)
+    a = 1.0 + 0.1 * normal((Hq * D,), seed + 4, torch.float32, DEV)
+    b = 0.1 * normal((Hq * D,), seed + 5, torch.float32, DEV)
+    ax = 1.0 + 0.1 * normal((Hq * D,), seed + 6, torch.float32, DEV)
+    bx = 0.1 * normal((Hq * D,), seed + 7, torch.float32, DEV)
+    d_o = normal((B, T, Hq, D), seed + 8, BF, DEV)
+    d_ox = normal((B, T_out, Hq, D), seed + 9, BF, DEV) if T_out else None
+    kc, vc, _ = make_cache(k, v, T)
+    o = torch.empty_like(q)
+    lo.orthros_swa_prefill(q, a, b, kc, vc, o, W, head_map=head_map)
+    ox = None
+    if T_out:
+        ox = torch.empty_like(qx)
+        lo.orthros_global_xattn(qx, ax, bx, kc, vc, ox, T - T_out,
+                                head_map=head_map)
+    g = lo.orthros_attn_backward(q, qx, a, b, ax, bx, kc, vc, o, ox, d_o,
+                                 d_ox, W, head_map=head_map)
+    torch.cuda.synchronize()
+    D_ = D
+    z = lambda t, shape: f64(t) if t is not None else np.zeros(shape)  # noqa
+    ref = oracle.attn_backward(
+        f64(q), z(qx, (B, 0, Hq, D_)), f64(a), f64(b), f64(ax), f64(bx),
+        f64(k), f64(v), f64(d_o), z(d_ox, (B, 0, Hq, D_)), W,
+        head_map=head_map)
+    return g, ref, T_out
+
+
+def check(g, ref, T_out):
+    names = ("dq_pre", "dk", "dv", "d_alpha", "d_beta")
+    if T_out:
+        names += ("dqx_pre", "d_alpha_x", "d_beta_x")
+    for name in names:
+        scale = max(1.0, float(np.abs(ref[name]).max()))
+        compare(g[name], ref[name], BF, f"{name} (largest {scale:.2f})",
+                tol=(TOL[BF][0] * scale, TOL[BF][1]))
+    if not T_out:
+        assert (f64(g["d_alpha_x"]) == 0).all() and (f64(g["d_beta_x"]) == 0).all()
+
+
+@pytest.mark.parametrize("B,T,T_out,Hq,Hkv,W", [
+    (2, 300, 3, 8, 2, 64),      # SFT-like, 4 query heads per KV head
+    (1, 257, 257, 4, 4, 100),   # pre-training: every position an output row
+    (1, 200, 0, 8, 1, 17),      # base stream only, 8 query heads per KV head
+    (1, 130, 5, 4, 2, 1000),    # window above T
+    (2, 97, 9, 4, 2, 1),        # window of one
+    (1, 700, 40, 8, 4, 129),    # several key tiles per row block
+])
+def test_backward_parity(B, T, T_out, Hq, Hkv, W):
+    say(f"[backward] B={B} T={T} T_out={T_out} Hq={Hq} Hkv={Hkv} W={W}")
+    check(*case(B, T, T_out, Hq, Hkv, W, 500 + T))
+
+
+def test_backward_custom_head_map():
+    hm = [2, 0, 1, 1, 0, 2]
+    say(f"[backward head map] {hm}")
+    check(*case(1, 150, 6, 6, 3, 33, 610, head_map=hm))
+
+
+def test_backward_deterministic():
+    a1, _, _ = case(1, 333, 7, 8, 2, 50, 620)
+    a2, _, _ = case(1, 333, 7, 8, 2, 50, 620)
+    for name in a1:
+        if a1[name] is not None:
+            x, y = a1[name], a2[name]
+            assert torch.equal(x.view(torch.int16) if x.dtype == BF else x.view(torch.int32),
+                               y.view(torch.int16) if y.dtype == BF else y.view(torch.int32)), name
