@@ -14,12 +14,12 @@ three prefill launches); the decode pair's KV GB/s and latency, the full
 causal run at the same T (speedup ratio), the roofline of the dominant
 kernel and the fp64 CPU oracle's rate on a bounded sample are reported
 beside it, with the sliding window at W = 128, the paged ragged decode and
-the whole layer (projections + attention + W_O) at 128K as extra legs
-outside the timed steps. All GPU times come from HIP events on the launch
+the whole layer (projections + attention + W_O) at 128K and the training
+backward at the SFT shape as extra legs outside the timed steps. All GPU times come from HIP events on the launch
 stream.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-causal]
-                [--no-paged] [--no-layer] [--no-cpu-baseline]
+                [--no-paged] [--no-layer] [--no-backward] [--no-cpu-baseline]
                 [--only prefill|decode]
 """
 import argparse
@@ -85,6 +85,7 @@ def main():
     ap.add_argument("--no-causal", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     args = ap.parse_args()
@@ -310,6 +311,10 @@ def main():
         out["layer_forward"] = layer_forward_leg(lo, pc, pc_id, kc4, vc4, dev,
                                                  ev)
 
+    # ---- training backward at the SFT shape (both streams) ------------------
+    if run_prefill and not args.no_backward:
+        out["backward_sft"] = backward_leg(lo, dev, ev)
+
     # ---- paged cache, ragged lengths (variable-length batched decoding) -----
     if run_decode and not args.no_paged:
         del kc3, vc3
@@ -322,6 +327,54 @@ def main():
         out["cpu_baseline"] = cpu_baseline(px, pc)
 
     print(json.dumps(out), flush=True)
+
+
+def backward_leg(lo, dev, ev, reps=2):
+    """orthros_attn_backward at the SFT dual-stream shape (B=4, T=8192,
+    T_out=2048, W=1024, 32/8 heads): forward outputs from the library, unit
+    upstream gradients. Algorithmic FLOPs: 8 D per (row, key) pair of either
+    stream (dV = P^T dO, dP = dO V^T, dQ = dS K, dK = dS^T Q); the score
+    recomputations are not counted."""
+    import torch
+
+    from workloads import normal, prefill_inputs, workload
+    c, cid = workload("sft_dual_8k")
+    x = prefill_inputs(c, cid, dev)
+    kc = torch.empty((c.B, c.Hkv, c.T, c.D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    cl = torch.zeros(c.B, dtype=torch.int32, device=dev)
+    lo.orthros_kv_append(kc, vc, cl, x.k, x.v)
+    o = torch.empty_like(x.q_pre)
+    ox = torch.empty_like(x.qx_pre)
+    lo.orthros_swa_prefill(x.q_pre, x.alpha, x.beta, kc, vc, o, c.W)
+    lo.orthros_global_xattn(x.qx_pre, x.alpha_x, x.beta_x, kc, vc, ox, c.T_in)
+    d_o = normal(tuple(o.shape), 9001, torch.bfloat16, dev)
+    d_ox = normal(tuple(ox.shape), 9002, torch.bfloat16, dev)
+    ws = lo.workspace(lo.orthros_backward_workspace_bytes(
+        c.B, c.T, c.T_out, c.Hq, c.Hkv, c.D), dev)
+    g = None
+
+    def f():
+        return lo.orthros_attn_backward(x.q_pre, x.qx_pre, x.alpha, x.beta,
+                                        x.alpha_x, x.beta_x, kc, vc, o, ox,
+                                        d_o, d_ox, c.W, out=g, ws=ws)
+    g = f()
+    torch.cuda.synchronize()
+    e0 = ev()
+    for _ in range(reps):
+        f()
+    e1 = ev()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps
+    pairs = band_pairs(c.T, c.W) + sum(c.T_in + r + 1 for r in range(c.T_out))
+    flop = 8.0 * c.D * pairs * c.Hq * c.B
+    res = {"workload": c.name, "ms": t, "tflops": flop / (t * 1e-3) / 1e12,
+           "algorithmic_tflop": flop / 1e12,
+           "mfma_frac": flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    log(f"[bench] backward {c.name}: {t:.2f} ms, {res['tflops']:.0f} TFLOP/s")
+    del x, kc, vc, o, ox, d_o, d_ox, ws, g
+    torch.cuda.empty_cache()
+    return res
 
 
 def layer_forward_leg(lo, pc, pc_id, kc, vc, dev, ev, reps=2):

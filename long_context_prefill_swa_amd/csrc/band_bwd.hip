@@ -20,9 +20,10 @@
 //    dQ^T += K^T dS^T (K^T read with ds_read_b64_tr_b16). It writes
 //    dq_pre, the row's log-sum-exp and dO . o, and per 32-row block the
 //    channel sums that make d alpha and d beta.
-//  * bwd_dkv_kernel (both streams): 4 waves, each 16 keys of one KV head,
-//    over every query head of that KV head and every 32-row block of either
-//    stream that sees the keys: S = Q K^T and dP = dO V^T with K, V held in
+//  * bwd_dkv_kernel (both streams): 8 waves, each 16 keys of one KV head,
+//    over every query head of that KV head and every 64-row block of either
+//    stream that sees the keys (16-row quarters outside a wave's band are
+//    skipped): S = Q K^T and dP = dO V^T with K, V held in
 //    registers, then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read
 //    transposed from LDS.
 //  * bwd_reduce_kernel: the per-block channel sums, added in a fixed order.
@@ -382,17 +383,23 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
 // ============================================================================
 // dK, dV of one KV head and 64 keys, over both streams
 // ============================================================================
+template <int GS>
 struct DkvSmem {
-  uint16_t q[32][kS];
-  uint16_t g[32][kS];
-  float lse[32], delta[32];
-  float ab[kMaxGroupSize][4][D];  // alpha, beta, alpha', beta' per head
+  uint16_t q[64][kS];
+  uint16_t g[64][kS];
+  float lse[64], delta[64];
+  float ab[GS][4][D];  // alpha, beta, alpha', beta' of the group's heads
 };
 
-__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdKvArgs a,
-                                                         HeadGroups groups) {
-  __shared__ __attribute__((aligned(16))) DkvSmem sm;
-  const int n_kt = (a.T + 63) / 64;
+constexpr int kKvWaves = 8;                 // 16 keys each
+constexpr int kKvKeys = 16 * kKvWaves;      // keys per workgroup
+constexpr int kKvThreads = 64 * kKvWaves;
+
+template <int GS>
+__global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
+    BwdKvArgs a, HeadGroups groups) {
+  __shared__ __attribute__((aligned(16))) DkvSmem<GS> sm;
+  const int n_kt = (a.T + kKvKeys - 1) / kKvKeys;
   const int kt = blockIdx.x % n_kt;
   const int rest = blockIdx.x / n_kt;
   const int gi = rest % groups.n_groups;  // the one group of this KV head
@@ -401,8 +408,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdKvArgs a,
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, g4 = lane >> 4, j16 = col;
-  const int k0 = kt * 64;
-  const int key = k0 + 16 * w + col;  // this lane's key (B columns)
+  const int k0 = kt * kKvKeys;
+  const int kw = k0 + 16 * w;          // first key of this wave
+  const int key = kw + col;            // this lane's key (B columns)
   const float qs = kLog2e * rsqrtf((float)D);
 
   // K and V rows of this wave's keys as B operands (channels 32 c4 + 8 g4)
@@ -420,26 +428,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdKvArgs a,
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) dk[dt] = dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Work list: (query head of this KV head) x (stream) x (32-row block).
+  // Work list: (query head of this KV head) x (stream) x (64-row block).
   const int T_in = a.T - a.T_out;
-  const int base_lo = (int)(k0 / 32);
-  const int base_hi = min(a.T - 1, k0 + 63 + a.W - 1) / 32;  // W <= T
+  const int base_lo = k0 / 64;
+  const int base_hi = min(a.T - 1, k0 + kKvKeys - 1 + a.W - 1) / 64;  // W <= T
   const int n_base = base_hi - base_lo + 1;
   int out_lo = 0, n_out = 0;
   if (a.T_out > 0) {
-    out_lo = max(0, k0 - T_in) / 32;
-    n_out = (a.T_out - 1) / 32 - out_lo + 1;
-    if (n_out < 0) n_out = 0;
+    out_lo = max(0, k0 - T_in) / 64;
+    n_out = max(0, (a.T_out - 1) / 64 - out_lo + 1);
   }
   const int per_head = n_base + n_out;
-
-  // query heads of this KV head: the group's slots up to the first empty one
-  int n_heads = 0;
-  while (n_heads < groups.gsize && groups.q[gi][n_heads] >= 0) ++n_heads;
+  int n_heads = 0;  // the group's slots up to the first empty one
+  while (n_heads < GS && groups.q[gi][n_heads] >= 0) ++n_heads;
   const int n_it = n_heads * per_head;
 
-  // alpha, beta of both streams for the group's heads, base-2 scale folded
-  for (int i = tid; i < n_heads * 4 * D; i += 256) {
+  for (int i = tid; i < n_heads * 4 * D; i += kKvThreads) {
     const int hi = i / (4 * D), which = (i / D) % 4, d = i % D;
     const float *src = which == 0 ? a.alpha : which == 1 ? a.beta
                      : which == 2 ? a.alpha_x : a.beta_x;
@@ -453,30 +457,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdKvArgs a,
     return Item{hi, s, s ? out_lo + (rr - n_base) : base_lo + rr};
   };
 
-  // staging: thread -> rows (tid / 16) and (tid / 16 + 16), one 16-byte
-  // chunk (8 channels) of each of Q and dO
+  // staging: thread -> rows tid/16 + 32 u (u = 0, 1), one 16-byte chunk;
+  // two register sets, so each block's loads are issued two blocks ahead
   const int srow = tid >> 4, sd0 = 8 * (tid & 15);
-  uint4 q0, q1, g0, g1;
-  float st_lse = 0.0f, st_delta = 0.0f;
-  auto load = [&](int it) {
+  struct Stage {
+    uint4 q0, q1, g0, g1;
+    float lse, delta;
+  };
+  auto load = [&](Stage &st, int it) {
     const Item itm = decode(it);
     const int h = groups.q[gi][itm.hi];
     const int nrows = itm.s ? a.T_out : a.T;
     const uint16_t *qsrc = itm.s ? a.qx : a.q;
     const uint16_t *gsrc = itm.s ? a.d_ox : a.d_o;
-    const int ra = min(itm.qb * 32 + srow, nrows - 1);
-    const int rb2 = min(itm.qb * 32 + srow + 16, nrows - 1);
-    const int64_t oa = (((int64_t)b * nrows + ra) * a.Hq + h) * D + sd0;
-    const int64_t ob = (((int64_t)b * nrows + rb2) * a.Hq + h) * D + sd0;
-    q0 = *(const uint4 *)(qsrc + oa);
-    g0 = *(const uint4 *)(gsrc + oa);
-    q1 = *(const uint4 *)(qsrc + ob);
-    g1 = *(const uint4 *)(gsrc + ob);
-    if (tid < 32) {
-      const int r = min(itm.qb * 32 + tid, nrows - 1);
+    auto off = [&](int u) {
+      const int r = min(itm.qb * 64 + srow + 16 * u, nrows - 1);
+      return (((int64_t)b * nrows + r) * a.Hq + h) * D + sd0;
+    };
+    const int64_t o0 = off(0), o1 = off(2);
+    st.q0 = *(const uint4 *)(qsrc + o0);
+    st.q1 = *(const uint4 *)(qsrc + o1);
+    st.g0 = *(const uint4 *)(gsrc + o0);
+    st.g1 = *(const uint4 *)(gsrc + o1);
+    if (tid < 64) {
+      const int r = min(itm.qb * 64 + tid, nrows - 1);
       const int64_t si = ((int64_t)b * a.Hq + h) * nrows + r;
-      st_lse = (itm.s ? a.lse_x : a.lse)[si];
-      st_delta = (itm.s ? a.delta_x : a.delta)[si];
+      st.lse = (itm.s ? a.lse_x : a.lse)[si];
+      st.delta = (itm.s ? a.delta_x : a.delta)[si];
     }
   };
   auto qrow = [&](uint4 raw, const float *al, const float *be) {
@@ -490,57 +497,87 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdKvArgs a,
     }
     return make_uint4(o4[0], o4[1], o4[2], o4[3]);
   };
-  auto store = [&](int it) {
+  auto store = [&](const Stage &st, int it) {
     const Item itm = decode(it);
     const float *al = sm.ab[itm.hi][2 * itm.s];
     const float *be = sm.ab[itm.hi][2 * itm.s + 1];
-    *(uint4 *)&sm.q[srow][sd0] = qrow(q0, al, be);
-    *(uint4 *)&sm.q[srow + 16][sd0] = qrow(q1, al, be);
-    *(uint4 *)&sm.g[srow][sd0] = g0;
-    *(uint4 *)&sm.g[srow + 16][sd0] = g1;
-    if (tid < 32) {
-      sm.lse[tid] = st_lse;
-      sm.delta[tid] = st_delta;
+    *(uint4 *)&sm.q[srow][sd0] = qrow(st.q0, al, be);
+    *(uint4 *)&sm.q[srow + 32][sd0] = qrow(st.q1, al, be);
+    *(uint4 *)&sm.g[srow][sd0] = st.g0;
+    *(uint4 *)&sm.g[srow + 32][sd0] = st.g1;
+    if (tid < 64) {
+      sm.lse[tid] = st.lse;
+      sm.delta[tid] = st.delta;
     }
   };
-
-  if (n_it > 0) load(0);
-  for (int it = 0; it < n_it; ++it) {
-    __syncthreads();
-    store(it);
-    __syncthreads();
-    if (it + 1 < n_it) load(it + 1);
+  auto block = [&](int it) {
     const Item itm = decode(it);
-    const int hi = itm.hi, s = itm.s, qb = itm.qb;
-    const int nrows = s ? a.T_out : a.T;
-    const int pos0 = (s ? T_in : 0) + qb * 32;  // position of row 0
-    const int Ws = s ? a.T : a.W;
-    bf16x8 pop, dsop;
+    const int nrows = itm.s ? a.T_out : a.T;
+    const int pos0 = (itm.s ? T_in : 0) + itm.qb * 64;  // position of row 0
+    const int Ws = itm.s ? a.T : a.W;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    for (int half = 0; half < 2; ++half) {  // rows 32 half .. + 31
+      bf16x8 pop, dsop;
 #pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        sc = mfma16(lds_row8(sm.q, 16 * h2 + col, c4, g4), kop[c4], sc);
-        dp = mfma16(lds_row8(sm.g, 16 * h2 + col, c4, g4), vop[c4], dp);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int rq0 = 32 * half + 16 * h2;  // first row of this quarter
+        // quarter entirely outside every (row, key) range of the wave?
+        const int p_lo = pos0 + rq0, p_hi = p_lo + 15;
+        const bool none = itm.qb * 64 + rq0 >= nrows || kw > p_hi ||
+                          kw + 15 < range_lo(p_lo, Ws) || kw >= a.T;
+        if (none) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pop[4 * h2 + i] = (__bf16)0.0f;
+            dsop[4 * h2 + i] = (__bf16)0.0f;
+          }
+          continue;
+        }
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          sc = mfma16(lds_row8(sm.q, rq0 + col, c4, g4), kop[c4], sc);
+          dp = mfma16(lds_row8(sm.g, rq0 + col, c4, g4), vop[c4], dp);
+        }
+        // every (row, key) of the quarter inside the ranges: no masking
+        const bool all_in = itm.qb * 64 + rq0 + 15 < nrows && kw + 15 < a.T &&
+                            kw + 15 <= p_lo && kw >= range_lo(p_hi, Ws);
+        // C rows are query rows rq0 + 4 g4 + i, the column is this key
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = rq0 + 4 * g4 + i;
+          const int p = pos0 + rl;
+          const bool ok = all_in || (itm.qb * 64 + rl < nrows && key < a.T &&
+                                     key <= p && key >= range_lo(p, Ws));
+          const float pr = ok ? __builtin_amdgcn_exp2f(sc[i] - sm.lse[rl]) : 0.0f;
+          pop[4 * h2 + i] = (__bf16)pr;
+          dsop[4 * h2 + i] = (__bf16)(pr * (dp[i] - sm.delta[rl]));
+        }
       }
-      // C rows are query rows 16 h2 + 4 g4 + i, the column is this key
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rl = 16 * h2 + 4 * g4 + i;
-        const int p = pos0 + rl;
-        const bool ok = qb * 32 + rl < nrows && key < a.T && key <= p &&
-                        key >= range_lo(p, Ws);
-        const float pr = ok ? __builtin_amdgcn_exp2f(sc[i] - sm.lse[rl]) : 0.0f;
-        pop[4 * h2 + i] = (__bf16)pr;
-        dsop[4 * h2 + i] = (__bf16)(pr * (dp[i] - sm.delta[rl]));
+      for (int dt = 0; dt < 8; ++dt) {
+        dv[dt] = mfma16(lds_tr8(sm.g, 32 * half, g4, j16, dt), pop, dv[dt]);
+        dk[dt] = mfma16(lds_tr8(sm.q, 32 * half, g4, j16, dt), dsop, dk[dt]);
       }
     }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      dv[dt] = mfma16(lds_tr8(sm.g, 0, g4, j16, dt), pop, dv[dt]);
-      dk[dt] = mfma16(lds_tr8(sm.q, 0, g4, j16, dt), dsop, dk[dt]);
-    }
+    };
+
+  // n_it >= 1: every group has a head and every key a base row
+  Stage sA = {}, sB = {};
+  load(sA, 0);
+  if (n_it > 1) load(sB, 1);
+  for (int it = 0; it < n_it; it += 2) {
+    __syncthreads();  // readers of the previous block are done (and ab)
+    store(sA, it);
+    __syncthreads();
+    if (it + 2 < n_it) load(sA, it + 2);
+    block(it);
+    if (it + 1 >= n_it) break;
+    __syncthreads();
+    store(sB, it + 1);
+    __syncthreads();
+    if (it + 3 < n_it) load(sB, it + 3);
+    block(it + 1);
   }
 
   // dK = dS^T (c q) / (c sqrt(D)) with c sqrt(D) = log2(e); dV = P^T dO
@@ -558,16 +595,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdKvArgs a,
   }
 }
 
-// d alpha, d beta [Hq*D] from the per-block sums [B, n_rb, Hq, 2, D].
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(
+// d alpha, d beta [Hq*D] from the per-block sums [B, n_rb, Hq, 2, D]: one
+// workgroup per (head, alpha|beta), 8 slices of the (batch, block) range per
+// channel, summed in a fixed order.
+__global__ __launch_bounds__(1024) void bwd_reduce_kernel(
     const float *__restrict__ part, float *__restrict__ d_alpha,
     float *__restrict__ d_beta, int B, int n_rb, int Hq) {
-  const int h = blockIdx.x, which = threadIdx.x / D, d = threadIdx.x % D;
-  float s = 0.0f;
-  for (int b = 0; b < B; ++b)
-    for (int r = 0; r < n_rb; ++r)
-      s += part[((((int64_t)b * n_rb + r) * Hq + h) * 2 + which) * D + d];
-  (which ? d_beta : d_alpha)[h * D + d] = s;
+  __shared__ float red[8][D];
+  const int h = blockIdx.x >> 1, which = blockIdx.x & 1;
+  const int d = threadIdx.x % D, sl = threadIdx.x / D;
+  const int n = B * n_rb, per = (n + 7) / 8;
+  const int i0 = sl * per, i1 = min(n, i0 + per);
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  int i = i0;
+  auto at = [&](int k) {
+    return part[(((int64_t)k * Hq + h) * 2 + which) * D + d];  // k = b n_rb + r
+  };
+  for (; i + 4 <= i1; i += 4) {
+    s0 += at(i);
+    s1 += at(i + 1);
+    s2 += at(i + 2);
+    s3 += at(i + 3);
+  }
+  for (; i < i1; ++i) s0 += at(i);
+  red[sl][d] = (s0 + s1) + (s2 + s3);
+  __syncthreads();
+  if (sl == 0) {
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += red[k][d];
+    (which ? d_beta : d_alpha)[h * D + d] = s;
+  }
 }
 
 }  // namespace
@@ -589,17 +647,22 @@ hipError_t launch_bwd_dq(const BwdStreamArgs &a, const HeadGroups &groups,
 
 hipError_t launch_bwd_dkv(const BwdKvArgs &a, const HeadGroups &groups,
                           int B, hipStream_t stream) {
-  const int n_kt = (a.T + 63) / 64;
-  hipLaunchKernelGGL(bwd_dkv_kernel,
-                     dim3((unsigned)(n_kt * groups.n_groups * B)), dim3(256), 0,
-                     stream, a, groups);
+  const int n_kt = (a.T + kKvKeys - 1) / kKvKeys;
+  const dim3 grid((unsigned)(n_kt * groups.n_groups * B)), blk(kKvThreads);
+  switch (groups.gsize) {
+    case 1: hipLaunchKernelGGL(bwd_dkv_kernel<1>, grid, blk, 0, stream, a, groups); break;
+    case 2: hipLaunchKernelGGL(bwd_dkv_kernel<2>, grid, blk, 0, stream, a, groups); break;
+    case 4: hipLaunchKernelGGL(bwd_dkv_kernel<4>, grid, blk, 0, stream, a, groups); break;
+    case 8: hipLaunchKernelGGL(bwd_dkv_kernel<8>, grid, blk, 0, stream, a, groups); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_reduce(const float *part, float *d_alpha, float *d_beta,
                              int B, int n_rb, int Hq, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(Hq), dim3(2 * D), 0, stream, part,
-                     d_alpha, d_beta, B, n_rb, Hq);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(2 * Hq), dim3(8 * D), 0, stream,
+                     part, d_alpha, d_beta, B, n_rb, Hq);
   return hipGetLastError();
 }
 
