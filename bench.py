@@ -42,6 +42,8 @@ BAND_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
                         "band_mfma.hip")
 SPLIT_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
                          "splitkv_mfma.hip")
+ROLL_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
+                        "band_roll.hip")
 
 
 def log(*a):
@@ -302,7 +304,15 @@ def main():
             "tflops": 4.0 * pc.D * band_pairs(pc.T, W_s) * pc.Hq * pc.B
             / (t_s * 1e-3) / 1e12,
             "algorithmic_bytes": by, "gbps": by / (t_s * 1e-3) / 1e9,
-            "hbm_frac": by / (t_s * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+            "hbm_frac": by / (t_s * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "roofline": {
+                "kernel": "band_roll_kernel (sliding window W=128, prefill_128k)",
+                "bound": "hbm", "achieved": by / (t_s * 1e-3) / 1e9,
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": by / (t_s * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                "traffic": traffic_from_profile("band_roll_prefill_128k_w128",
+                                                kernel_sha(ROLL_SRC)),
+                "kernel_source_sha256": kernel_sha(ROLL_SRC)}}
         log(f"[bench] swa W=128: {t_s:.3f} ms, "
             f"{out['swa_w128']['gbps']:.0f} GB/s")
 
