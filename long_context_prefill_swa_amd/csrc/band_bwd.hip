@@ -517,41 +517,63 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     const int Ws = itm.s ? a.T : a.W;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {  // rows 32 half .. + 31
-      bf16x8 pop, dsop;
+      bool none[2], all_in[2];
+      float4 lse4[2], del4[2];
+      f32x4 sc[2], dp[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int rq0 = 32 * half + 16 * h2;  // first row of this quarter
-        // quarter entirely outside every (row, key) range of the wave?
         const int p_lo = pos0 + rq0, p_hi = p_lo + 15;
-        const bool none = itm.qb * 64 + rq0 >= nrows || kw > p_hi ||
-                          kw + 15 < range_lo(p_lo, Ws) || kw >= a.T;
-        if (none) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pop[4 * h2 + i] = (__bf16)0.0f;
-            dsop[4 * h2 + i] = (__bf16)0.0f;
-          }
-          continue;
-        }
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+        // quarter entirely outside every (row, key) range of the wave, or
+        // entirely inside (no masking)
+        none[h2] = itm.qb * 64 + rq0 >= nrows || kw > p_hi ||
+                   kw + 15 < range_lo(p_lo, Ws) || kw >= a.T;
+        all_in[h2] = itm.qb * 64 + rq0 + 15 < nrows && kw + 15 < a.T &&
+                     kw + 15 <= p_lo && kw >= range_lo(p_hi, Ws);
+        // row statistics of C rows rq0 + 4 g4 .. + 3, read up front
+        lse4[h2] = *(const float4 *)&sm.lse[rq0 + 4 * g4];
+        del4[h2] = *(const float4 *)&sm.delta[rq0 + 4 * g4];
+        sc[h2] = dp[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      auto quarter = [&](int h2) {
+        const int rq0 = 32 * half + 16 * h2;
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
-          sc = mfma16(lds_row8(sm.q, rq0 + col, c4, g4), kop[c4], sc);
-          dp = mfma16(lds_row8(sm.g, rq0 + col, c4, g4), vop[c4], dp);
+          sc[h2] = mfma16(lds_row8(sm.q, rq0 + col, c4, g4), kop[c4], sc[h2]);
+          dp[h2] = mfma16(lds_row8(sm.g, rq0 + col, c4, g4), vop[c4], dp[h2]);
         }
-        // every (row, key) of the quarter inside the ranges: no masking
-        const bool all_in = itm.qb * 64 + rq0 + 15 < nrows && kw + 15 < a.T &&
-                            kw + 15 <= p_lo && kw >= range_lo(p_hi, Ws);
+      };
+      if (!none[0] && !none[1]) {
+        quarter(0);
+        quarter(1);
+        // operand reads run ahead of the 16 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+      } else {
+        if (!none[0]) quarter(0);
+        if (!none[1]) quarter(1);
+      }
+      bf16x8 pop, dsop;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int rq0 = 32 * half + 16 * h2;
+        const float lv[4] = {lse4[h2].x, lse4[h2].y, lse4[h2].z, lse4[h2].w};
+        const float dv4[4] = {del4[h2].x, del4[h2].y, del4[h2].z, del4[h2].w};
         // C rows are query rows rq0 + 4 g4 + i, the column is this key
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rl = rq0 + 4 * g4 + i;
           const int p = pos0 + rl;
-          const bool ok = all_in || (itm.qb * 64 + rl < nrows && key < a.T &&
-                                     key <= p && key >= range_lo(p, Ws));
-          const float pr = ok ? __builtin_amdgcn_exp2f(sc[i] - sm.lse[rl]) : 0.0f;
+          const bool ok = !none[h2] &&
+                          (all_in[h2] || (itm.qb * 64 + rl < nrows && key < a.T &&
+                                          key <= p && key >= range_lo(p, Ws)));
+          const float pr = ok ? __builtin_amdgcn_exp2f(sc[h2][i] - lv[i]) : 0.0f;
           pop[4 * h2 + i] = (__bf16)pr;
-          dsop[4 * h2 + i] = (__bf16)(pr * (dp[i] - sm.delta[rl]));
+          dsop[4 * h2 + i] = (__bf16)(pr * (dp[h2][i] - dv4[i]));
         }
       }
 #pragma unroll
@@ -559,8 +581,15 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
         dv[dt] = mfma16(lds_tr8(sm.g, 32 * half, g4, j16, dt), pop, dv[dt]);
         dk[dt] = mfma16(lds_tr8(sm.q, 32 * half, g4, j16, dt), dsop, dk[dt]);
       }
+      // transposed reads run two MFMAs ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
     }
-    };
+  };
 
   // n_it >= 1: every group has a head and every key a base row
   Stage sA = {}, sB = {};
