@@ -209,19 +209,26 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
   }
 
   // S^T block (16 keys of sub-block kb x 16 rows of half h2), masked
-  auto scores = [&](int kt, int kb, int h2) {
+  auto scores_raw = [&](int kb, int h2) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4)
       s = mfma16(lds_row8(sm.k, 16 * kb + col, c4, g4), qop[h2][c4], s);
-    // key kept iff lo <= key <= p, i.e. (unsigned)(key - lo) <= p - lo
+    return s;
+  };
+  // key kept iff lo <= key <= p, i.e. (unsigned)(key - lo) <= p - lo
+  auto mask = [&](f32x4 &s, int kt, int kb, int h2) {
     const int lo = range_lo(prow[h2], a.W);
     const uint32_t u0 = (uint32_t)(kt * 64 + 16 * kb + 4 * g4 - lo);
     const uint32_t span = (uint32_t)(prow[h2] - lo);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s[i] = (u0 + i <= span) ? s[i] : -INFINITY;
-    return s;
+    for (int i = 0; i < 4; ++i) s[i] = (u0 + i <= span) ? s[i] : -INFINITY;
+  };
+  // tile inside every row's range of this wave (valid rows only): no mask
+  const int p_w_valid_last = p_w_last;
+  auto tile_inside = [&](int kt) {
+    return kt * 64 >= range_lo(p_w_valid_last, a.W) && kt * 64 + 63 <= p_w_first &&
+           r0 + 32 <= a.nrows;
   };
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
@@ -250,16 +257,26 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
     next_tile(kt);
     load(kt < kt_hi ? kt + 1 : kt_lo);  // pass 2 starts over at kt_lo
     if (!wave_needs(kt)) continue;
+    const bool inside = tile_inside(kt);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       f32x4 s[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = scores_raw(kb, h2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (!inside)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) mask(s[kb], kt, kb, h2);
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = scores(kt, kb, h2);
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kb][i]);
-      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mn = fmaxf(m[h2], tmax);
@@ -287,31 +304,49 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
     next_tile(kt);
     if (kt < kt_hi) load(kt + 1);
     if (!wave_needs(kt)) continue;
+    const bool inside = tile_inside(kt);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        bf16x8 dsop;
+        f32x4 sv[2], dp[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int kb = 2 * kp + half;
-          const f32x4 s = scores(kt, kb, h2);
-          f32x4 dp = {0.f, 0.f, 0.f, 0.f};
+          sv[half] = scores_raw(kb, h2);
+          dp[half] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4)
-            dp = mfma16(lds_row8(sm.v, 16 * kb + col, c4, g4), doop[h2][c4], dp);
+            dp[half] = mfma16(lds_row8(sm.v, 16 * kb + col, c4, g4), doop[h2][c4], dp[half]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        bf16x8 dsop;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          if (!inside) mask(sv[half], kt, 2 * kp + half, h2);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // masked keys (and rows with no key at all) give p = 0
-            const float p = s[i] == -INFINITY
+            const float p = sv[half][i] == -INFINITY
                                 ? 0.0f
-                                : __builtin_amdgcn_exp2f(s[i] - lse[h2]);
-            dsop[4 * half + i] = (__bf16)(p * (dp[i] - delta[h2]));
+                                : __builtin_amdgcn_exp2f(sv[half][i] - lse[h2]);
+            dsop[4 * half + i] = (__bf16)(p * (dp[half][i] - delta[h2]));
           }
         }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
           acc[h2][dt] = mfma16(lds_tr8(sm.k, 32 * kp, g4, j16, dt), dsop, acc[h2][dt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
