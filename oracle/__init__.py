@@ -19,6 +19,9 @@ names the passage of the pages it follows:
 * ``attn_backward`` gradients of both streams (q_pre, qx_pre, K, V and the
                   four scale-offset vectors) for training (paper text §3.2,
                   pre-training and SFT), row by row in numpy fp64
+* ``attn_backward_sampled`` selected rows' dq and selected keys' dK, dV of
+                  the same gradients, in matrix form over the rows that see
+                  each key (for full-size checks)
 * ``layer``       one attention layer with its projections: k, v = x W_K,
                   x W_V for the base rows, q = alpha (.) (x W_Q) + beta and
                   q' = alpha' (.) (x' W_Q) + beta', the two streams, their
@@ -332,3 +335,76 @@ def attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k, v, d_o,
     for name in ("d_alpha", "d_beta", "d_alpha_x", "d_beta_x"):
         g[name] = g[name].reshape(-1)
     return g
+
+
+def attn_backward_sampled(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k, v,
+                          d_o, d_ox, W, b, rows, out_rows, keys, g):
+    """Selected entries of ``attn_backward`` for one batch entry b, fp64.
+
+    rows / out_rows: base positions t / output rows r whose dq_pre / dqx_pre
+    (all heads) are returned; keys: key positions j whose dK, dV for KV head
+    g (contiguous head grouping) are returned. Every gradient is the same
+    chain rule; a row's softmax is taken over its whole key range (matrix
+    products over the rows that see the sampled keys, masked).
+    Returns (dq [len(rows), Hq, D], dqx [len(out_rows), Hq, D],
+    dk [len(keys), D], dv [len(keys), D]).
+    """
+    q_pre, qx_pre = _f64(q_pre[b]), _f64(qx_pre[b])
+    kb, vb = _f64(k[b]), _f64(v[b])
+    d_o, d_ox = _f64(d_o[b]), _f64(d_ox[b])
+    T, Hq, D = q_pre.shape
+    Hkv = kb.shape[1]
+    T_out = qx_pre.shape[0]
+    T_in = T - T_out
+    G = Hq // Hkv
+    scale = 1.0 / np.sqrt(D)
+    A, Bv = _f64(alpha).reshape(Hq, D), _f64(beta).reshape(Hq, D)
+    AX, BX = _f64(alpha_x).reshape(Hq, D), _f64(beta_x).reshape(Hq, D)
+    pos = np.arange(T)
+
+    def grads(Q, dO, p_row, lo_row, kv):
+        """Rows Q [n, D] at positions p_row with ranges [lo_row, p_row]
+        against all keys of KV head kv: P, dS [n, T] (zero outside)."""
+        K, V = kb[:, kv], vb[:, kv]
+        s = Q @ K.T * scale
+        inside = (pos[None, :] >= lo_row[:, None]) & (pos[None, :] <= p_row[:, None])
+        s = np.where(inside, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        dp = dO @ V.T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        return p, ds
+
+    dq = np.zeros((len(rows), Hq, D))
+    dqx = np.zeros((len(out_rows), Hq, D))
+    for h in range(Hq):
+        kv = h // G
+        if len(rows):
+            t = np.asarray(rows)
+            Q = A[h] * q_pre[t, h] + Bv[h]
+            _, ds = grads(Q, d_o[t, h], t, np.maximum(t - W + 1, 0), kv)
+            dq[:, h] = A[h] * (ds @ kb[:, kv] * scale)
+        if len(out_rows):
+            r = np.asarray(out_rows)
+            Q = AX[h] * qx_pre[r, h] + BX[h]
+            p_ = T_in + r
+            _, ds = grads(Q, d_ox[r, h], p_, np.zeros_like(p_), kv)
+            dqx[:, h] = AX[h] * (ds @ kb[:, kv] * scale)
+    dk = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    for h in range(g * G, (g + 1) * G):
+        for n, j in enumerate(keys):
+            t = np.arange(j, min(T, j + W))          # base rows that see j
+            if len(t):
+                Q = A[h] * q_pre[t, h] + Bv[h]
+                p, ds = grads(Q, d_o[t, h], t, np.maximum(t - W + 1, 0), g)
+                dk[n] += ds[:, j] @ Q * scale
+                dv[n] += p[:, j] @ d_o[t, h]
+            r = np.arange(max(0, j - T_in), T_out)   # output rows that see j
+            if len(r):
+                Q = AX[h] * qx_pre[r, h] + BX[h]
+                p_ = T_in + r
+                p, ds = grads(Q, d_ox[r, h], p_, np.zeros_like(p_), g)
+                dk[n] += ds[:, j] @ Q * scale
+                dv[n] += p[:, j] @ d_ox[r, h]
+    return dq, dqx, dk, dv

@@ -95,3 +95,44 @@ def test_backward_deterministic():
             x, y = a1[name], a2[name]
             assert torch.equal(x.view(torch.int16) if x.dtype == BF else x.view(torch.int32),
                                y.view(torch.int16) if y.dtype == BF else y.view(torch.int32)), name
+
+
+def test_backward_sft_shape_sampled():
+    """The SFT dual-stream shape the benchmark times (B=4, T=8192,
+    T_out=2048, W=1024, 32/8 heads): dq_pre on sampled base rows and dqx_pre
+    on sampled output rows (all heads), dK and dV on sampled keys of KV
+    head 0, for the first and last batch entries. (The scale-offset
+    gradients sum over every row; they are checked at the smaller shapes.)"""
+    from workloads import prefill_inputs, workload
+    c, cid = workload("sft_dual_8k")
+    say(f"[backward full size] {c.name}")
+    x = prefill_inputs(c, cid, DEV)
+    kc, vc, _ = make_cache(x.k, x.v, c.T)
+    o = torch.empty_like(x.q_pre)
+    ox = torch.empty_like(x.qx_pre)
+    lo.orthros_swa_prefill(x.q_pre, x.alpha, x.beta, kc, vc, o, c.W)
+    lo.orthros_global_xattn(x.qx_pre, x.alpha_x, x.beta_x, kc, vc, ox, c.T_in)
+    d_o = normal(tuple(o.shape), 9001, BF, DEV)
+    d_ox = normal(tuple(ox.shape), 9002, BF, DEV)
+    g = lo.orthros_attn_backward(x.q_pre, x.qx_pre, x.alpha, x.beta,
+                                 x.alpha_x, x.beta_x, kc, vc, o, ox, d_o,
+                                 d_ox, c.W)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    rows = sorted({0, 1, c.W - 1, c.W, c.T_in - 1, c.T_in, c.T - 1,
+                   *map(int, rng.integers(0, c.T, 6))})
+    out_rows = sorted({0, 1, c.T_out - 1, *map(int, rng.integers(0, c.T_out, 3))})
+    keys = [0, 1000, c.T_in, c.T - 1]
+    args = [f64(t) for t in (x.q_pre, x.qx_pre, x.alpha, x.beta, x.alpha_x,
+                             x.beta_x, x.k, x.v, d_o, d_ox)]
+    for b in (0, c.B - 1):
+        dq, dqx, dk, dv = oracle.attn_backward_sampled(*args, c.W, b, rows,
+                                                       out_rows, keys, 0)
+        for name, got, ref in (
+                ("dq_pre", g["dq_pre"][b, rows], dq),
+                ("dqx_pre", g["dqx_pre"][b, out_rows], dqx),
+                ("dk", g["dk"][b, keys, 0], dk),
+                ("dv", g["dv"][b, keys, 0], dv)):
+            scale = max(1.0, float(np.abs(ref).max()))
+            compare(got, ref, BF, f"b={b} {name} (largest {scale:.2f})",
+                    tol=(TOL[BF][0] * scale, TOL[BF][1]))

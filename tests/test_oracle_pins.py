@@ -583,3 +583,20 @@ def test_backward_finite_differences():
             minus[i][idx] -= eps
             fd = (loss(*plus) - loss(*minus)) / (2 * eps)
             assert abs(fd - g[name][idx]) < 1e-6, (name, idx, fd, g[name][idx])
+
+
+def test_backward_sampled_equals_full():
+    """The sampled backward (matrix form over the rows that see each key)
+    equals the row-by-row one on every sampled entry."""
+    B, T, T_out, Hq, Hkv, D, W = 2, 40, 7, 4, 2, 8, 9
+    args = grad_case(B, T, T_out, Hq, Hkv, D, 811)
+    full = oracle.attn_backward(*args, W)
+    rows, out_rows, keys = [0, 5, 8, 9, 39], [0, 3, 6], [0, 4, 30, 33, 39]
+    for b in range(B):
+        for g in range(Hkv):
+            dq, dqx, dk, dv = oracle.attn_backward_sampled(
+                *args, W, b, rows, out_rows, keys, g)
+            np.testing.assert_allclose(dq, full["dq_pre"][b, rows], atol=1e-12)
+            np.testing.assert_allclose(dqx, full["dqx_pre"][b, out_rows], atol=1e-12)
+            np.testing.assert_allclose(dk, full["dk"][b, keys, g], atol=1e-12)
+            np.testing.assert_allclose(dv, full["dv"][b, keys, g], atol=1e-12)
