@@ -17,9 +17,8 @@ LIB = os.path.join(HERE, "liborthros.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kv_append.hip", "rowwise.hip", "splitkv_mfma.hip",
-           "band_mfma.hip", "band_roll.hip", "band_bwd.hip", "orthros_api.cpp",
-           "gemm.cpp",
-           "layer.cpp"]
+           "band_mfma.hip", "band_roll.hip", "band_persist.hip",
+           "band_bwd.hip", "orthros_api.cpp", "gemm.cpp", "layer.cpp"]
 
 # Packed fp32 instructions stay off: hipcc is asked not to form them.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -125,6 +125,15 @@ hipError_t launch_bwd_dkv(const BwdKvArgs &a, const HeadGroups &groups,
 hipError_t launch_bwd_reduce(const float *part, float *d_alpha, float *d_beta,
                              int B, int n_rb, int Hq, hipStream_t stream);
 
+// Persistent banded attention (bf16, D = 128, 4 query heads per KV head,
+// bounded window W >= 1): workgroups walk runs of 64-row query tiles.
+hipError_t launch_band_persist(const void *q, const float *alpha,
+                               const float *beta, const void *k_cache,
+                               const void *v_cache, void *o, int B, int nrows,
+                               int Hq, int64_t cap, int W,
+                               const HeadGroups &groups, int n_kv,
+                               hipStream_t stream);
+
 // Rolling-window attention for small windows, bf16, D = 128, 4 query heads
 // per KV head, rows at positions 0 .. nrows-1, 1 <= W <= kRollMaxWindow.
 constexpr int kRollMaxWindow = 129;

@@ -176,6 +176,41 @@ def test_swa_rolling_padded_group():
             dt, "swa")
 
 
+# --- base stream: persistent banded kernel (4 query heads per KV head,
+# 129 < W <= T/4) ---------------------------------------------------------------
+
+@pytest.mark.parametrize("B,T,Hq,Hkv,W", [
+    (2, 3000, 8, 2, 300),     # ragged tail, window not a tile multiple
+    (1, 5000, 8, 2, 1000),
+    (1, 4097, 32, 8, 513),    # eight groups, one row past a tile
+    (1, 2048, 8, 2, 512),     # tile multiples
+    (3, 700, 8, 2, 130),      # smallest window of this path
+])
+def test_swa_persistent_parity(B, T, Hq, Hkv, W):
+    D = 128
+    say(f"[swa persistent] B={B} T={T} Hq={Hq} Hkv={Hkv} W={W}")
+    dt = torch.bfloat16
+    q, k, v = rand((B, T, Hq, D), 40, dt), rand((B, T, Hkv, D), 41, dt), rand((B, T, Hkv, D), 42, dt)
+    a, b = affine_pair(Hq * D, 43)
+    o = run_swa(q, a, b, k, v, W)
+    compare(o, oracle_swa(q, a, b, k, v, W), dt, "swa")
+
+
+def test_swa_persistent_padded_group():
+    """A head map whose groups hold 3 and 2 query heads (padded to 4): the
+    padded slots' rows are computed on clamped copies and never stored."""
+    hmap = [0, 1, 0, 1, 0]
+    B, T, D, Hkv, W = 2, 1500, 128, 2, 300
+    Hq = len(hmap)
+    say(f"[swa persistent head map] {hmap}")
+    dt = torch.bfloat16
+    q, k, v = rand((B, T, Hq, D), 44, dt), rand((B, T, Hkv, D), 45, dt), rand((B, T, Hkv, D), 46, dt)
+    a, b = affine_pair(Hq * D, 47)
+    o = run_swa(q, a, b, k, v, W, head_map=hmap)
+    compare(o, oracle_swa(q, a, b, k, v, W, head_map=np.array(hmap, np.int32)),
+            dt, "swa")
+
+
 @pytest.mark.parametrize("hmap", [[2, 0, 1, 1, 0, 2], [0, 0, 0, 1, 2, 2]])
 def test_swa_custom_head_map(hmap):
     B, T, D, Hkv = 2, 200, 128, 3
