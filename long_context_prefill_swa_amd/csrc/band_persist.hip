@@ -41,6 +41,7 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr float kTau = 8.0f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct Tiles {
   uint16_t k[2][kBN][kKS];
@@ -78,6 +79,16 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_base) {
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+}
+
+// The lane id, recomputed where it is used: per-lane addresses needed only
+// between items are rebuilt from it instead of being kept (or spilled)
+// across the tile loop, which needs every VGPR.
+__device__ __forceinline__ int fresh_lane() {
+  int ln;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0"
+               : "=v"(ln));
+  return ln;
 }
 
 __device__ __forceinline__ void wait_all_vm() {
@@ -134,28 +145,49 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   // (a row of the four heads is 1 KB, contiguous when the heads are). Rows
   // past the end and padded head slots are loaded as copies of valid rows
   // (clamped) and never stored.
-  const int slot_head = groups.q[gi][lane >> 4];
-  const int hq_of_lane = max(slot_head, 0);
+  const int gq0 = groups.q[gi][0], gq1 = groups.q[gi][1];
+  const int gq2 = groups.q[gi][2], gq3 = groups.q[gi][3];
+  auto slot_head_of = [&](int ln) __attribute__((always_inline)) {
+    const int sl = ln >> 4;
+    return sl == 0 ? gq0 : sl == 1 ? gq1 : sl == 2 ? gq2 : gq3;
+  };
   auto load_qblock = [&](int qt) __attribute__((always_inline)) {
+    const int ln = fresh_lane();
+    const int hq = max(slot_head_of(ln), 0);
 #pragma unroll
     for (int rr = 0; rr < kItemRows / kNW; ++rr) {
       const int row = (kItemRows / kNW) * w + rr;
       const int r = min(qt * kItemRows + row, nrows - 1);
       const uint16_t *src =
-          q + (((int64_t)b * nrows + r) * Hq + hq_of_lane) * D + 8 * (lane & 15);
+          q + (((int64_t)b * nrows + r) * Hq + hq) * D + 8 * (ln & 15);
       lds_dma16(src, __builtin_amdgcn_readfirstlane(
                          (uint32_t)(uintptr_t)(lds_void *)&qsm.qb[row][0]));
     }
   };
+  // The output rows of item qt go through a buffer resource that covers just
+  // the item's valid rows; padded head slots aim past its end. Out-of-range
+  // stores are dropped by the hardware, so no lane branches, and all eight
+  // rows are read from LDS before the first store (distinct registers: no
+  // store waits on the one before it).
   auto store_oblock = [&](int qt) __attribute__((always_inline)) {
+    const int ln = fresh_lane();
+    const int sh = slot_head_of(ln);
+    const uint32_t slot_off =
+        sh >= 0 ? (uint32_t)(sh * D + 8 * (ln & 15)) * 2u : 0x80000000u;
+    const int r0 = qt * kItemRows;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        o + ((int64_t)b * nrows + r0) * Hq * D, 0,
+        (uint32_t)(min(kItemRows, nrows - r0) * Hq * D * 2), kBufferWord3);
+    uint4 val[kItemRows / kNW];
+#pragma unroll
+    for (int rr = 0; rr < kItemRows / kNW; ++rr)
+      val[rr] = *(const uint4 *)&sm.ob[(kItemRows / kNW) * w + rr][8 * ln];
 #pragma unroll
     for (int rr = 0; rr < kItemRows / kNW; ++rr) {
       const int row = (kItemRows / kNW) * w + rr;
-      const int r = qt * kItemRows + row;
-      const uint4 val = *(const uint4 *)&sm.ob[row][8 * lane];
-      if (slot_head >= 0 && r < nrows)
-        *(uint4 *)(o + (((int64_t)b * nrows + r) * Hq + hq_of_lane) * D +
-                   8 * (lane & 15)) = val;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, val[rr]), ro, slot_off,
+          __builtin_amdgcn_readfirstlane(row * Hq * D * 2), 0);
     }
   };
 
@@ -240,12 +272,13 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     // ---- query operand from the block in LDS (B of S^T) --------------------
     bf16x8 qop[8];
     {
-      const uint16_t *qrow = &qsm.qb[kRows * ps + j][hs * D];
+      const int ln = fresh_lane();
+      const uint16_t *qrow = &qsm.qb[kRows * ps + (ln & 31)][hs * D];
       const float *al = sm.ab[hs][0];
       const float *be = sm.ab[hs][1];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const int d0 = 16 * c + 8 * hh;
+        const int d0 = 16 * c + 8 * (ln >> 5);
         const uint4 raw = *(const uint4 *)(qrow + d0);
         const uint32_t wv[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -406,13 +439,18 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     // Normalise this wave's rows into the output block over the K/V tiles
     // (free after the last step's barrier) and write it out as whole rows.
     {
-      const float inv = 1.0f / (l + __shfl_xor(l, 32, 64));
-      uint16_t *orow = &sm.ob[kRows * ps + j][hs * D];
+      // row sum: this lane's half plus its partner's (lane ^ 32)
+      const auto lp = __builtin_amdgcn_permlane32_swap(
+          __float_as_uint(l), __float_as_uint(l), false, false);
+      const float inv =
+          1.0f / (__uint_as_float(lp[0]) + __uint_as_float(lp[1]));
+      const int ln = fresh_lane();
+      uint16_t *orow = &sm.ob[kRows * ps + (ln & 31)][hs * D];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = 32 * dt + 8 * q4 + 4 * hh;
+          const int d0 = 32 * dt + 8 * q4 + 4 * (ln >> 5);
           uint32_t pk[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
