@@ -39,7 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 BAND_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
-                        "band_mfma.hip")
+                        "band_persist.hip")
 SPLIT_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
                          "splitkv_mfma.hip")
 ROLL_SRC = os.path.join(ROOT, "long_context_prefill_swa_amd", "csrc",
@@ -232,10 +232,10 @@ def main():
         }
         sha = kernel_sha(BAND_SRC)
         out["roofline"] = {
-            "kernel": "band_mfma_kernel (sliding-window prefill, prefill_128k)",
+            "kernel": "band_persist_kernel (sliding-window prefill, prefill_128k)",
             "bound": "mfma", "achieved": swa_tflops, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": swa_tflops / PEAK_BF16_TFLOPS,
-            "traffic": traffic_from_profile("band_mfma_prefill_128k", sha),
+            "traffic": traffic_from_profile("band_persist_prefill_128k", sha),
             "algorithmic_flop_per_launch": F_swa,
             "avg_launch_ms": t_swa, "kernel_source_sha256": sha}
         log(f"[bench] prefill: append {t_app:.3f} ms, swa {t_swa:.3f} ms "
