@@ -403,13 +403,17 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   }
 }
 
-// One workgroup per (row, head group, batch). Thread (q, part): chunks
-// c_lo + q, c_lo + q + 16, ... and channels 8 part .. 8 part + 7; the 16
+// One workgroup per (row, head group, batch). Thread (q, part) = (tid / 4,
+// tid % 4): chunks c_lo + q, c_lo + q + 64, ... and channels 32 part ..
+// 32 part + 31. Every load of a chunk is issued before its maximum is
+// tested, so a row over up to 64 chunks costs one memory round trip; the 64
 // chunk lanes are then combined in LDS.
+constexpr int kMergeLanes = 64;
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
                                                             HeadGroups groups) {
-  __shared__ float sm_m[16], sm_l[16];
-  __shared__ float sm_acc[16][D + 4];
+  __shared__ float sm_m[kMergeLanes], sm_l[kMergeLanes], sm_f[kMergeLanes];
+  __shared__ float sm_sum;
+  __shared__ float sm_acc[kMergeLanes][D + 4];
   const int r = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int gsize = groups.gsize;
@@ -431,8 +435,11 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
     ((int32_t *)a.cache_len)[b] = (int32_t)(n_old + 1);
   if (h < 0) return;
 
-  const int q = tid >> 4, part = tid & 15, d0 = 8 * part;
-  float M = -INFINITY, L = 0.0f, o8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int q = tid >> 2, part = tid & 3, d0 = 32 * part;
+  float M = -INFINITY, L = 0.0f;
+  f32x4 o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t t = (a.cache_len ? n_old : a.pos0) + j;
   int c_lo = 0, c_hi = -1;
   if (ok) {
@@ -441,57 +448,62 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
     c_lo = (int)(lo / a.chunk);
     c_hi = (int)(t / a.chunk);
   }
-  for (int cc = c_lo + q; cc <= c_hi; cc += 16) {
+  for (int cc = c_lo + q; cc <= c_hi; cc += kMergeLanes) {
     const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, cc, r);
     const float mc = a.ws[pi * 2];
-    if (mc == -INFINITY) continue;
     const float lc = a.ws[pi * 2 + 1];
-    const float *pacc = a.ws + (int64_t)a.ws_acc_offset + pi * D + d0;
-    const float4 u = *(const float4 *)pacc;
-    const float4 v = *(const float4 *)(pacc + 4);
-    const float Mn = fmaxf(M, mc);
-    const float fo = exp2f(M - Mn), fn = exp2f(mc - Mn);
-    L = L * fo + lc * fn;
-    const float pv[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    const f32x4 *pacc =
+        (const f32x4 *)(a.ws + (int64_t)a.ws_acc_offset + pi * D + d0);
+    f32x4 u[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o8[e] = o8[e] * fo + pv[e] * fn;
-    M = Mn;
+    for (int k = 0; k < 8; ++k) u[k] = pacc[k];
+    if (mc != -INFINITY) {  // a chunk with keys in this row's range
+      const float Mn = fmaxf(M, mc);
+      const float fo = exp2f(M - Mn), fn = exp2f(mc - Mn);
+      L = L * fo + lc * fn;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = o[k] * fo + u[k] * fn;
+      M = Mn;
+    }
   }
   if (part == 0) {
     sm_m[q] = M;
     sm_l[q] = L;
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sm_acc[q][d0 + e] = o8[e];
+  for (int k = 0; k < 8; ++k) *(f32x4 *)&sm_acc[q][d0 + 4 * k] = o[k];
   __syncthreads();
-  if (tid < 16) {
-    // thread `part` = tid combines the 16 chunk lanes for channels 8 tid..
-    float Mx = -INFINITY;
+  if (tid < kMergeLanes) {
+    // wave 0: the row maximum over the lanes, each lane's weight, and the sum
+    const float mq = sm_m[tid];
+    float Mx = mq;
 #pragma unroll
-    for (int qq = 0; qq < 16; ++qq) Mx = fmaxf(Mx, sm_m[qq]);
-    float Lx = 0.0f, out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (Mx != -INFINITY) {
+    for (int sh = 32; sh >= 1; sh >>= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, sh, 64));
+    const float f = (mq == -INFINITY) ? 0.0f : exp2f(mq - Mx);
+    sm_f[tid] = f;
+    float lsum = f * sm_l[tid];
 #pragma unroll
-      for (int qq = 0; qq < 16; ++qq) {
-        const float f = exp2f(sm_m[qq] - Mx);
-        Lx += f * sm_l[qq];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] += f * sm_acc[qq][8 * tid + e];
-      }
-      const float inv = 1.0f / Lx;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] *= inv;
+    for (int sh = 32; sh >= 1; sh >>= 1) lsum += __shfl_xor(lsum, sh, 64);
+    if (tid == 0) sm_sum = lsum;
+  }
+  __syncthreads();
+  if (tid < D / 2) {
+    // thread tid: channels 2 tid, 2 tid + 1
+    float out0 = 0.0f, out1 = 0.0f;
+#pragma unroll 8
+    for (int qq = 0; qq < kMergeLanes; ++qq) {
+      const float f = sm_f[qq];
+      const float2 v = *(const float2 *)&sm_acc[qq][2 * tid];
+      out0 += f * v.x;
+      out1 += f * v.y;
     }
-    uint32_t pk[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo16 = __builtin_bit_cast(uint16_t, (__bf16)out[2 * e]);
-      const uint32_t hi16 = __builtin_bit_cast(uint16_t, (__bf16)out[2 * e + 1]);
-      pk[e] = lo16 | (hi16 << 16);
-    }
+    const float Lx = sm_sum;
+    const float inv = Lx > 0.0f ? 1.0f / Lx : 0.0f;
+    const uint32_t lo16 = __builtin_bit_cast(uint16_t, (__bf16)(out0 * inv));
+    const uint32_t hi16 = __builtin_bit_cast(uint16_t, (__bf16)(out1 * inv));
     uint16_t *dst = (uint16_t *)a.o[s] +
-                    (((int64_t)b * a.n_pos + j) * a.Hq + h) * D + 8 * tid;
-    *(uint4 *)dst = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                    (((int64_t)b * a.n_pos + j) * a.Hq + h) * D + 2 * tid;
+    *(uint32_t *)dst = lo16 | (hi16 << 16);
   }
 }
 
