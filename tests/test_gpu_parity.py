@@ -196,6 +196,28 @@ def test_swa_persistent_parity(B, T, Hq, Hkv, W):
     compare(o, oracle_swa(q, a, b, k, v, W), dt, "swa")
 
 
+def test_swa_persistent_many_heads_sampled():
+    """More (batch, KV head) pairs than compute units: each workgroup walks
+    every query tile of its pair. Rows at tile boundaries of the first,
+    middle and last batch entries, plus random ones."""
+    B, T, Hq, Hkv, D, W = 40, 600, 32, 8, 128, 150
+    say(f"[swa persistent many heads] B={B} T={T} W={W}")
+    dt = torch.bfloat16
+    q, k, v = rand((B, T, Hq, D), 48, dt), rand((B, T, Hkv, D), 49, dt), rand((B, T, Hkv, D), 50, dt)
+    a, b = affine_pair(Hq * D, 51)
+    o = run_swa(q, a, b, k, v, W)
+    rows = set()
+    for bb in (0, B // 2, B - 1):
+        for e in range(0, T, 64):
+            rows.update((bb, t) for t in (e - 1, e, e + 63) if 0 <= t < T)
+    rng = np.random.default_rng(52)
+    rows.update((int(x), int(y)) for x, y in zip(rng.integers(0, B, 100), rng.integers(0, T, 100)))
+    rows = np.array(sorted(rows), np.int64)
+    ref = oracle_swa(q, a, b, k, v, W, rows=rows)
+    got = torch.stack([o[bb, t] for bb, t in rows])
+    compare(got, ref, dt, f"swa ({len(rows)} rows)")
+
+
 def test_swa_persistent_padded_group():
     """A head map whose groups hold 3 and 2 query heads (padded to 4): the
     padded slots' rows are computed on clamped copies and never stored."""
