@@ -474,15 +474,16 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     n_out = max(0, (a.T_out - 1) / 64 - out_lo + 1);
   }
   const int per_head = n_base + n_out;
+  const GroupHeads gh = group_heads(groups, gi);
   int n_heads = 0;  // the group's slots up to the first empty one
-  while (n_heads < GS && groups.q[gi][n_heads] >= 0) ++n_heads;
+  while (n_heads < GS && slot_head(gh, n_heads) >= 0) ++n_heads;
   const int n_it = n_heads * per_head;
 
   for (int i = tid; i < n_heads * 4 * D; i += kKvThreads) {
     const int hi = i / (4 * D), which = (i / D) % 4, d = i % D;
     const float *src = which == 0 ? a.alpha : which == 1 ? a.beta
                      : which == 2 ? a.alpha_x : a.beta_x;
-    sm.ab[hi][which][d] = src[groups.q[gi][hi] * D + d] * qs;
+    sm.ab[hi][which][d] = src[slot_head(gh, hi) * D + d] * qs;
   }
 
   struct Item { int hi, s, qb; };
@@ -501,7 +502,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
   };
   auto load = [&](Stage &st, int it) {
     const Item itm = decode(it);
-    const int h = groups.q[gi][itm.hi];
+    const int h = slot_head(gh, itm.hi);
     const int nrows = itm.s ? a.T_out : a.T;
     const uint16_t *qsrc = itm.s ? a.qx : a.q;
     const uint16_t *gsrc = itm.s ? a.d_ox : a.d_o;
@@ -514,12 +515,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     st.q1 = *(const uint4 *)(qsrc + o1);
     st.g0 = *(const uint4 *)(gsrc + o0);
     st.g1 = *(const uint4 *)(gsrc + o1);
-    if (tid < 64) {
-      const int r = min(itm.qb * 64 + tid, nrows - 1);
-      const int64_t si = ((int64_t)b * a.Hq + h) * nrows + r;
-      st.lse = (itm.s ? a.lse_x : a.lse)[si];
-      st.delta = (itm.s ? a.delta_x : a.delta)[si];
-    }
+    // every thread loads (only the first 64 store): the same loads on
+    // every path keep the waits before the LDS stores exact
+    const int r = min(itm.qb * 64 + (tid & 63), nrows - 1);
+    const int64_t si = ((int64_t)b * a.Hq + h) * nrows + r;
+    st.lse = (itm.s ? a.lse_x : a.lse)[si];
+    st.delta = (itm.s ? a.delta_x : a.delta)[si];
   };
   auto qrow = [&](uint4 raw, const float *al, const float *be) {
     const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -626,22 +627,30 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     }
   };
 
-  // n_it >= 1: every group has a head and every key a base row
+  // n_it >= 1: every group has a head and every key a base row. Loads
+  // past the last block re-read it (unused), so that every block issues the
+  // same loads; a counted loop of block pairs keeps one path through it.
   Stage sA = {}, sB = {};
   load(sA, 0);
-  if (n_it > 1) load(sB, 1);
-  for (int it = 0; it < n_it; it += 2) {
+  load(sB, min(1, n_it - 1));
+  int it = 0;
+  for (; it + 1 < n_it; it += 2) {
     __syncthreads();  // readers of the previous block are done (and ab)
     store(sA, it);
     __syncthreads();
-    if (it + 2 < n_it) load(sA, it + 2);
+    load(sA, min(it + 2, n_it - 1));
     block(it);
-    if (it + 1 >= n_it) break;
     __syncthreads();
     store(sB, it + 1);
     __syncthreads();
-    if (it + 3 < n_it) load(sB, it + 3);
+    load(sB, min(it + 3, n_it - 1));
     block(it + 1);
+  }
+  if (it < n_it) {
+    __syncthreads();
+    store(sA, it);
+    __syncthreads();
+    block(it);
   }
 
   // dK = dS^T (c q) / (c sqrt(D)) with c sqrt(D) = log2(e); dV = P^T dO

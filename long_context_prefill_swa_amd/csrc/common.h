@@ -20,6 +20,23 @@ struct HeadGroups {
   int8_t q[kMaxGroups][kMaxGroupSize];
 };
 
+// The query heads of group gi packed in two dwords (slot s in bits
+// 8 (s % 4) .. 8 (s % 4) + 7 of word s / 4). A kernel argument read one byte
+// at a time is a vector load, and its wait also waits for every load in
+// flight; the dwords are scalar loads.
+struct GroupHeads {
+  uint32_t w[2];
+};
+__device__ __forceinline__ GroupHeads group_heads(const HeadGroups &g, int gi) {
+  const uint32_t *p = (const uint32_t *)&g.q[gi][0];
+  return GroupHeads{{p[0], p[1]}};
+}
+// Query head of slot s (0 .. 7), or -1 for an empty slot.
+__device__ __forceinline__ int slot_head(const GroupHeads &h, int s) {
+  const uint32_t w = s < 4 ? h.w[0] : h.w[1];
+  return (int)(int8_t)(w >> (8 * (s & 3)));
+}
+
 // Plain per-query-head map (generic kernels).
 struct HeadMap {
   uint8_t kv_of_q[kMaxHeads];
