@@ -273,9 +273,9 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
                          cap, W, groups, Hkv, as_stream(stream));
   } else if (mfma_eligible(dtype, D, T,
                            {q_pre, alpha, beta, k_cache, v_cache, o}) &&
-             groups.gsize == 4 && (int64_t)W * 4 <= T) {
-    // bounded window of at most a quarter of the rows: resident workgroups
-    // walk runs of query tiles (persistent kernel)
+             groups.gsize == 4) {
+    // larger windows (up to the whole prefix): resident workgroups walk
+    // runs of query tiles (persistent kernel)
     e = launch_band_persist(q_pre, alpha, beta, k_cache, v_cache, o, B, T,
                             Hq, cap, W, groups, Hkv, as_stream(stream));
   } else if (mfma_eligible(dtype, D, T,

@@ -177,7 +177,7 @@ def test_swa_rolling_padded_group():
 
 
 # --- base stream: persistent banded kernel (4 query heads per KV head,
-# 129 < W <= T/4) ---------------------------------------------------------------
+# W > 129) ----------------------------------------------------------------------
 
 @pytest.mark.parametrize("B,T,Hq,Hkv,W", [
     (2, 3000, 8, 2, 300),     # ragged tail, window not a tile multiple
@@ -185,6 +185,9 @@ def test_swa_rolling_padded_group():
     (1, 4097, 32, 8, 513),    # eight groups, one row past a tile
     (1, 2048, 8, 2, 512),     # tile multiples
     (3, 700, 8, 2, 130),      # smallest window of this path
+    (1, 1000, 8, 2, 1000),    # window = T (full causal)
+    (2, 777, 8, 2, 5000),     # window above T
+    (1, 2000, 8, 2, 1500),    # window above T / 4
 ])
 def test_swa_persistent_parity(B, T, Hq, Hkv, W):
     D = 128
