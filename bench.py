@@ -403,9 +403,10 @@ def layer_forward_leg(lo, pc, pc_id, kc, vc, dev, ev, reps=2):
     HqD, HkvD = pc.Hq * pc.D, pc.Hkv * pc.D
     gemm_flop = 2.0 * B * (M * dm * HqD * 2 + pc.T * dm * HkvD * 2)
     res = {"d_model": dm, "gemm_tflop": gemm_flop / 1e12}
+    wq, wk, wv, wo = x.stored_weights()
     for W in (pc.W, 128):
         def f():
-            lo.orthros_layer_forward(x.x, x.w_q, x.w_k, x.w_v, x.w_o, x.alpha,
+            lo.orthros_layer_forward(x.x, wq, wk, wv, wo, x.alpha,
                                      x.beta, x.alpha_x, x.beta_x, kc, vc, cl,
                                      y, pc.T_out, W, ws=ws)
         f()

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 4
+#define ORTHROS_ABI_VERSION 5
 
 /* dtype codes */
 #define ORTHROS_F32 0
@@ -344,9 +344,10 @@ size_t orthros_backward_workspace_bytes(int B, int T, int T_out, int Hq,
  * other entry points. Query heads map to KV heads contiguously (h / (Hq/Hkv)).
  *
  *   x           [dev] [B, T + T_out, d_model] bf16
- *   w_q         [dev] [d_model, Hq*D] bf16 (row-major: x W_Q)
- *   w_k, w_v    [dev] [d_model, Hkv*D] bf16
- *   w_o         [dev] [Hq*D, d_model] bf16
+ *   w_q         [dev] [Hq*D, d_model] bf16: W_Q stored out x in (row j holds
+ *               column j of W_Q), the layout of a linear layer's weight
+ *   w_k, w_v    [dev] [Hkv*D, d_model] bf16, the same way
+ *   w_o         [dev] [d_model, Hq*D] bf16, the same way
  *   alpha, beta, alpha_x, beta_x [dev] fp32 [Hq*D] (the _x pair may be NULL
  *               when T_out = 0)
  *   k_cache, v_cache [dev] [B, Hkv, cap, D] bf16, rows 0..T-1 written

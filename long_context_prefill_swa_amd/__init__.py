@@ -366,19 +366,20 @@ def orthros_layer_workspace_bytes(B, T, T_out, d_model, Hq, Hkv, D):
 def orthros_layer_forward(x, w_q, w_k, w_v, w_o, alpha, beta, alpha_x,
                           beta_x, k_cache, v_cache, cache_len, y, T_out, W,
                           ws=None, stream=None):
-    """x, y [B, T+T_out, d_model]; w_q [d_model, Hq*D]; w_k, w_v
-    [d_model, Hkv*D]; w_o [Hq*D, d_model]; caches [B, Hkv, cap, D]."""
+    """x, y [B, T+T_out, d_model]; weights stored out x in (a linear
+    layer's weight): w_q [Hq*D, d_model], w_k, w_v [Hkv*D, d_model],
+    w_o [d_model, Hq*D]; caches [B, Hkv, cap, D]."""
     B, M, d_model = x.shape
     T = M - int(T_out)
     Hkv, cap, D = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
-    Hq = w_q.shape[1] // D
+    Hq = w_q.shape[0] // D
     if tuple(k_cache.shape) != (B, Hkv, cap, D) or v_cache.shape != k_cache.shape:
         raise ValueError("k_cache/v_cache must be [B, Hkv, cap, D]")
-    if (tuple(w_q.shape) != (d_model, Hq * D) or
-            tuple(w_k.shape) != (d_model, Hkv * D) or w_v.shape != w_k.shape or
-            tuple(w_o.shape) != (Hq * D, d_model)):
-        raise ValueError("weights must be [d_model, Hq*D], [d_model, Hkv*D] "
-                         "x2 and [Hq*D, d_model]")
+    if (tuple(w_q.shape) != (Hq * D, d_model) or
+            tuple(w_k.shape) != (Hkv * D, d_model) or w_v.shape != w_k.shape or
+            tuple(w_o.shape) != (d_model, Hq * D)):
+        raise ValueError("weights must be [Hq*D, d_model], [Hkv*D, d_model] "
+                         "x2 and [d_model, Hq*D]")
     if y.shape != x.shape:
         raise ValueError("y must have x's shape")
     if ws is None:

@@ -16,7 +16,8 @@
 #include "common.h"
 
 namespace orthros {
-int gemm_bf16(const void *A, const void *B, void *C, int64_t M, int64_t N,
+// C[M, N] = A[M, K] Wt[N, K]^T, row-major bf16 (weights stored out x in).
+int gemm_bf16(const void *A, const void *Wt, void *C, int64_t M, int64_t N,
               int64_t K, void *ws, size_t ws_bytes, hipStream_t stream,
               char *msg, size_t msg_len);
 int api_error(int code, const char *msg);

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.orthros_abi_version() == 4
+    assert L.orthros_abi_version() == 5
     for code in (OK, EINVAL, EUNSUP, ECAP, EWS, EHIP):
         assert L.orthros_strerror(code)
     assert b"unknown" in L.orthros_strerror(42)

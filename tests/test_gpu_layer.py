@@ -24,7 +24,8 @@ def run_layer(cfg, cfg_id, W=None, d_model=None, cap=None, len_before=7):
     vc = torch.full_like(kc, float("nan"))
     cl = torch.full((B,), len_before, dtype=torch.int32, device=DEV)
     y = torch.empty_like(x.x)
-    lo.orthros_layer_forward(x.x, x.w_q, x.w_k, x.w_v, x.w_o, x.alpha, x.beta,
+    wq, wk, wv, wo = x.stored_weights()
+    lo.orthros_layer_forward(x.x, wq, wk, wv, wo, x.alpha, x.beta,
                              x.alpha_x, x.beta_x, kc, vc, cl, y, cfg.T_out, W)
     torch.cuda.synchronize()
     lo.orthros_check_device_errors()

@@ -189,6 +189,12 @@ class LayerInputs:
     alpha_x: torch.Tensor
     beta_x: torch.Tensor
 
+    def stored_weights(self):
+        """The four weights stored out x in (a linear layer's layout, the
+        form the layer entry point takes): contiguous transposes."""
+        return tuple(w.t().contiguous()
+                     for w in (self.w_q, self.w_k, self.w_v, self.w_o))
+
 
 def scaled_normal(shape, seed: int, fan_in: int, dtype, device="cpu"):
     """N(0, 1) / sqrt(fan_in), drawn in fp32, then rounded to `dtype`."""
@@ -200,8 +206,9 @@ def scaled_normal(shape, seed: int, fan_in: int, dtype, device="cpu"):
 
 def layer_inputs(cfg: Config, cfg_id: int, d_model: Optional[int] = None,
                  device="cpu") -> LayerInputs:
-    """Inputs of one layer forward: hidden rows, the four weights, the
-    affine vectors (bf16 tensors, fp32 affine)."""
+    """Inputs of one layer forward: hidden rows, the four weights as the
+    matrices of x W (stored_weights() gives them out x in), the affine
+    vectors (bf16 tensors, fp32 affine)."""
     dm = cfg.Hq * cfg.D if d_model is None else d_model
     s = lambda name: seed_of(cfg_id, name)  # noqa: E731
     bf = torch.bfloat16
