@@ -13,14 +13,15 @@ The reported value is prefill tokens/s (B*T over the summed time of the
 three prefill launches); the decode pair's KV GB/s and latency, the full
 causal run at the same T (speedup ratio), the roofline of the dominant
 kernel and the fp64 CPU oracle's rate on a bounded sample are reported
-beside it, with the sliding window at W = 128, the paged ragged decode and
-the whole layer (projections + attention + W_O) at 128K and the training
-backward at the SFT shape as extra legs outside the timed steps. All GPU times come from HIP events on the launch
+beside it. Extra legs outside the timed steps: the sliding window at
+W = 128, the paged ragged decode, the whole layer (projections + attention
++ W_O) at 128K, the 32K and SFT dual-stream prefills, and the training
+backward at the SFT shape. All GPU times come from HIP events on the launch
 stream.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-causal]
-                [--no-paged] [--no-layer] [--no-backward] [--no-cpu-baseline]
-                [--only prefill|decode]
+                [--no-paged] [--no-layer] [--no-backward] [--no-other-prefills]
+                [--no-cpu-baseline] [--only prefill|decode]
 """
 import argparse
 import hashlib
@@ -88,6 +89,7 @@ def main():
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--no-layer", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-other-prefills", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None)
     args = ap.parse_args()
@@ -321,6 +323,12 @@ def main():
         out["layer_forward"] = layer_forward_leg(lo, pc, pc_id, kc4, vc4, dev,
                                                  ev)
 
+    # ---- the other prefill shapes: 32K single layer, SFT dual stream -------
+    if run_prefill and not args.no_other_prefills:
+        out["other_prefills"] = {
+            name: prefill_leg(lo, name, dev, ev)
+            for name in ("prefill_32k", "sft_dual_8k")}
+
     # ---- training backward at the SFT shape (both streams) ------------------
     if run_prefill and not args.no_backward:
         out["backward_sft"] = backward_leg(lo, dev, ev)
@@ -384,6 +392,63 @@ def backward_leg(lo, dev, ev, reps=2):
     log(f"[bench] backward {c.name}: {t:.2f} ms, {res['tflops']:.0f} TFLOP/s")
     del x, kc, vc, o, ox, d_o, d_ox, ws, g
     torch.cuda.empty_cache()
+    return res
+
+
+def global_pairs(T, T_out):
+    """(query, key) pairs of the output stream per head: output row r sits
+    at position T - T_out + r and sees every key up to it."""
+    T_in = T - T_out
+    return T_out * T_in + T_out * (T_out + 1) // 2
+
+
+def prefill_leg(lo, name, dev, ev, reps=5):
+    """One prefill of workload `name` (cache fill, sliding window, output
+    stream), its attention TFLOP/s and tokens/s."""
+    import torch
+    from workloads import prefill_inputs, workload
+    c, cid = workload(name)
+    x = prefill_inputs(c, cid, dev)
+    kc = torch.empty((c.B, c.Hkv, c.T, c.D), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    cl = torch.zeros(c.B, dtype=torch.int32, device=dev)
+    o = torch.empty_like(x.q_pre)
+    ox = torch.empty_like(x.qx_pre)
+    ws = lo.workspace(lo.orthros_workspace_bytes(
+        lo.ORTHROS_OP_GLOBAL_XATTN, c.B, c.Hq, c.Hkv, c.D, c.T_out, c.T), dev)
+
+    def run(marks):
+        cl.zero_()
+        marks.append(ev())
+        lo.orthros_kv_append(kc, vc, cl, x.k, x.v)
+        marks.append(ev())
+        lo.orthros_swa_prefill(x.q_pre, x.alpha, x.beta, kc, vc, o, c.W)
+        marks.append(ev())
+        lo.orthros_global_xattn(x.qx_pre, x.alpha_x, x.beta_x, kc, vc, ox,
+                                c.T_in, ws=ws)
+        marks.append(ev())
+    run([])
+    torch.cuda.synchronize()
+    recs = []
+    for _ in range(reps):
+        m = []
+        run(m)
+        recs.append(m)
+    torch.cuda.synchronize()
+    t = [sum(r[i].elapsed_time(r[i + 1]) for r in recs) / reps for i in range(3)]
+    F_swa = 4.0 * c.D * band_pairs(c.T, c.W) * c.Hq * c.B
+    F_glob = 4.0 * c.D * global_pairs(c.T, c.T_out) * c.Hq * c.B
+    res = {"config": f"B={c.B} Hq={c.Hq} Hkv={c.Hkv} D={c.D} T={c.T} "
+                     f"W={c.W} T_out={c.T_out}",
+           "ms_kv_append": t[0], "ms_swa": t[1], "ms_global": t[2],
+           "tokens_per_s": c.B * c.T / (sum(t) * 1e-3),
+           "swa_tflops": F_swa / (t[1] * 1e-3) / 1e12,
+           "global_tflops": F_glob / (t[2] * 1e-3) / 1e12,
+           "attention_tflops": (F_swa + F_glob) / ((t[1] + t[2]) * 1e-3) / 1e12}
+    res["attention_frac_of_bf16_peak"] = res["attention_tflops"] / PEAK_BF16_TFLOPS
+    log(f"[bench] {name}: append {t[0]:.3f} ms, swa {t[1]:.3f} ms, "
+        f"global {t[2]:.3f} ms, attention {res['attention_tflops']:.0f} TFLOP/s")
+    del kc, vc, x
     return res
 
 

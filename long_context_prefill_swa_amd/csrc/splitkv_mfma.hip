@@ -403,17 +403,21 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   }
 }
 
-// One workgroup per (row, head group, batch). Thread (q, part) = (tid / 4,
-// tid % 4): chunks c_lo + q, c_lo + q + 64, ... and channels 32 part ..
-// 32 part + 31. Every load of a chunk is issued before its maximum is
-// tested, so a row over up to 64 chunks costs one memory round trip; the 64
-// chunk lanes are then combined in LDS.
-constexpr int kMergeLanes = 64;
+// One workgroup per (row, head group, batch), LANES chunk lanes of
+// 256 / LANES threads. Thread (q, part): chunks c_lo + q, c_lo + q + LANES,
+// ... and channels CH part .. CH part + CH - 1 (CH = D LANES / 256). Every
+// load of a chunk is issued before its maximum is tested, so a row over up
+// to LANES chunks costs one memory round trip; the lanes are then combined
+// in LDS. 64 lanes serve rows over more than 32 chunks (a long prompt's
+// output row); 16 lanes, with a quarter of the LDS and so more resident
+// workgroups, serve the decode step's rows over a few.
+template <int LANES>
 __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
                                                             HeadGroups groups) {
-  __shared__ float sm_m[kMergeLanes], sm_l[kMergeLanes], sm_f[kMergeLanes];
+  constexpr int kParts = 256 / LANES, CH = D / kParts;
+  __shared__ float sm_m[LANES], sm_l[LANES], sm_f[LANES];
   __shared__ float sm_sum;
-  __shared__ float sm_acc[kMergeLanes][D + 4];
+  __shared__ float sm_acc[LANES][D + 4];
   const int r = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int gsize = groups.gsize;
@@ -435,11 +439,11 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
     ((int32_t *)a.cache_len)[b] = (int32_t)(n_old + 1);
   if (h < 0) return;
 
-  const int q = tid >> 2, part = tid & 3, d0 = 32 * part;
+  const int q = tid / kParts, part = tid % kParts, d0 = CH * part;
   float M = -INFINITY, L = 0.0f;
-  f32x4 o[8];
+  f32x4 o[CH / 4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < CH / 4; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t t = (a.cache_len ? n_old : a.pos0) + j;
   int c_lo = 0, c_hi = -1;
   if (ok) {
@@ -448,21 +452,21 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
     c_lo = (int)(lo / a.chunk);
     c_hi = (int)(t / a.chunk);
   }
-  for (int cc = c_lo + q; cc <= c_hi; cc += kMergeLanes) {
+  for (int cc = c_lo + q; cc <= c_hi; cc += LANES) {
     const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, cc, r);
     const float mc = a.ws[pi * 2];
     const float lc = a.ws[pi * 2 + 1];
     const f32x4 *pacc =
         (const f32x4 *)(a.ws + (int64_t)a.ws_acc_offset + pi * D + d0);
-    f32x4 u[8];
+    f32x4 u[CH / 4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) u[k] = pacc[k];
+    for (int k = 0; k < CH / 4; ++k) u[k] = pacc[k];
     if (mc != -INFINITY) {  // a chunk with keys in this row's range
       const float Mn = fmaxf(M, mc);
       const float fo = exp2f(M - Mn), fn = exp2f(mc - Mn);
       L = L * fo + lc * fn;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] = o[k] * fo + u[k] * fn;
+      for (int k = 0; k < CH / 4; ++k) o[k] = o[k] * fo + u[k] * fn;
       M = Mn;
     }
   }
@@ -471,19 +475,21 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
     sm_l[q] = L;
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) *(f32x4 *)&sm_acc[q][d0 + 4 * k] = o[k];
+  for (int k = 0; k < CH / 4; ++k) *(f32x4 *)&sm_acc[q][d0 + 4 * k] = o[k];
   __syncthreads();
-  if (tid < kMergeLanes) {
-    // wave 0: the row maximum over the lanes, each lane's weight, and the sum
+  if (tid < LANES) {
+    // the first LANES threads: the row maximum over the lanes, each lane's
+    // weight, and the sum (xor shuffles within the LANES-wide group)
     const float mq = sm_m[tid];
     float Mx = mq;
 #pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, sh, 64));
+    for (int sh = LANES / 2; sh >= 1; sh >>= 1)
+      Mx = fmaxf(Mx, __shfl_xor(Mx, sh, 64));
     const float f = (mq == -INFINITY) ? 0.0f : exp2f(mq - Mx);
     sm_f[tid] = f;
     float lsum = f * sm_l[tid];
 #pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) lsum += __shfl_xor(lsum, sh, 64);
+    for (int sh = LANES / 2; sh >= 1; sh >>= 1) lsum += __shfl_xor(lsum, sh, 64);
     if (tid == 0) sm_sum = lsum;
   }
   __syncthreads();
@@ -491,7 +497,7 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
     // thread tid: channels 2 tid, 2 tid + 1
     float out0 = 0.0f, out1 = 0.0f;
 #pragma unroll 8
-    for (int qq = 0; qq < kMergeLanes; ++qq) {
+    for (int qq = 0; qq < LANES; ++qq) {
       const float f = sm_f[qq];
       const float2 v = *(const float2 *)&sm_acc[qq][2 * tid];
       out0 += f * v.x;
@@ -556,8 +562,12 @@ hipError_t launch_splitkv(const SplitKVArgs &a_in, const HeadGroups &groups,
                        a, groups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(splitkv_merge_kernel, dim3(rows, groups.n_groups, a.B),
-                     dim3(256), 0, stream, a, groups);
+  if (a.n_chunks > 32)
+    hipLaunchKernelGGL(splitkv_merge_kernel<64>, dim3(rows, groups.n_groups, a.B),
+                       dim3(256), 0, stream, a, groups);
+  else
+    hipLaunchKernelGGL(splitkv_merge_kernel<16>, dim3(rows, groups.n_groups, a.B),
+                       dim3(256), 0, stream, a, groups);
   return hipGetLastError();
 }
 
