@@ -15,8 +15,8 @@
 // workgroups of a KV head work on neighbouring tiles whose bands share the
 // XCD's L2. Per item:
 //  * the query block (64 rows x 4 heads) was brought into LDS by direct
-//    global-to-LDS loads (global_load_lds_dwordx4) issued during the
-//    previous item;
+//    global-to-LDS loads (global_load_lds_dwordx4) issued early in the
+//    previous item's tile loop;
 //  * the first K/V tiles were requested before the previous item's output
 //    was written;
 //  * the tile loop is the banded kernel's;
@@ -362,7 +362,12 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     store_v(ra, 0);
     load_tile(cur, ra, 2);
     __syncthreads();  // tiles in LDS; every wave has read the query block
-    if (n < n_last) load_qblock(seg + (n + 1) * n_segs);
+    // The next item's query block: issued at the start of the second loop
+    // iteration when there is one (its address work then overlaps the
+    // step's MFMAs, and it is older than that step's tile loads, whose wait
+    // gives it a whole step), else here.
+    const bool q_in_loop = ntiles >= 4;
+    if (n < n_last && !q_in_loop) load_qblock(seg + (n + 1) * n_segs);
     f32x16 sa[2], sb[2];
     scores(sa, 0);
     settle(sa, kt0 * kBN);
@@ -421,6 +426,8 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     };
     int it = 0;
     for (; it + 1 < ntiles; it += 2) {
+      if (it == 2 && q_in_loop && n < n_last)
+        load_qblock(seg + (n + 1) * n_segs);
       step(sa, sb, ra, rb, it);
       step(sb, sa, rb, ra, it + 1);
     }
