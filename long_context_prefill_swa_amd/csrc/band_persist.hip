@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ alpha,
     const float *__restrict__ beta, const uint16_t *__restrict__ k_cache,
     const uint16_t *__restrict__ v_cache, uint16_t *__restrict__ o,
-    int nrows, int Hq, int n_kv, int64_t cap, int W, int n_qtiles,
+    int nrows, int pos_off, int Hq, int n_kv, int64_t cap, int W, int n_qtiles,
     int n_segs, HeadGroups groups) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   __shared__ __attribute__((aligned(16))) QBlock qsm;
@@ -199,12 +199,14 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   auto item_of = [&](int n) __attribute__((always_inline)) {
     Item it;
     it.qt = seg + n * n_segs;
+    // rows r0 .. r0 + 63 sit at positions pos_off + r0 ...
     const int r0 = it.qt * kItemRows;
-    const int k_hi = min(r0 + kItemRows, nrows) - 1;
-    it.kt0 = max(0, r0 - W + 1) / kBN;
+    const int p0 = pos_off + r0;
+    const int k_hi = pos_off + min(r0 + kItemRows, nrows) - 1;
+    it.kt0 = max(0, p0 - W + 1) / kBN;
     it.ntiles = k_hi / kBN - it.kt0 + 1;
-    it.wpos_lo = r0 + kRows * ps;
-    it.wpos_hi = min(it.wpos_lo + kRows, nrows) - 1;
+    it.wpos_lo = p0 + kRows * ps;
+    it.wpos_hi = pos_off + min(r0 + kRows * ps + kRows, nrows) - 1;
     // Cache slab of this (batch, KV head), read through buffer resources
     // that end after key k_hi: tile rows past it load as zeros.
     const uint32_t slab_bytes = (uint32_t)(k_hi + 1) * (D * 2);
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     const int64_t kt0 = cur.kt0;
     const int ntiles = cur.ntiles;
     const int wpos_lo = cur.wpos_lo, wpos_hi = cur.wpos_hi;
-    const int tq = wpos_lo + j;  // this lane's query row
+    const int tq = wpos_lo + j;  // this lane's query position
 
     float m = -INFINITY, l = 0.0f;
     f32x16 acc[4], negm;
@@ -479,13 +481,15 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
 }  // namespace
 
 // Workgroups of the persistent kernel: about one per compute unit, each on
-// every n_segs-th query tile of one (batch, KV head).
+// every n_segs-th query tile of one (batch, KV head). W <= 0: every key up
+// to the row's position.
 hipError_t launch_band_persist(const void *q, const float *alpha,
                                const float *beta, const void *k_cache,
                                const void *v_cache, void *o, int B, int nrows,
-                               int Hq, int64_t cap, int W,
+                               int pos_off, int Hq, int64_t cap, int W,
                                const HeadGroups &groups, int n_kv,
                                hipStream_t stream) {
+  if (W <= 0) W = pos_off + nrows;
   const int n_qtiles = (nrows + kItemRows - 1) / kItemRows;
   int dev = 0, n_cu = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -499,7 +503,7 @@ hipError_t launch_band_persist(const void *q, const float *alpha,
   hipLaunchKernelGGL(band_persist_kernel, dim3((unsigned)(n_segs * per)),
                      dim3(kNT), 0, stream, (const uint16_t *)q, alpha, beta,
                      (const uint16_t *)k_cache, (const uint16_t *)v_cache,
-                     (uint16_t *)o, nrows, Hq, n_kv, cap, W, n_qtiles,
+                     (uint16_t *)o, nrows, pos_off, Hq, n_kv, cap, W, n_qtiles,
                      (int)n_segs, groups);
   return hipGetLastError();
 }

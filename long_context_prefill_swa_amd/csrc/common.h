@@ -142,12 +142,14 @@ hipError_t launch_bwd_dkv(const BwdKvArgs &a, const HeadGroups &groups,
 hipError_t launch_bwd_reduce(const float *part, float *d_alpha, float *d_beta,
                              int B, int n_rb, int Hq, hipStream_t stream);
 
-// Persistent banded attention (bf16, D = 128, 4 query heads per KV head,
-// bounded window W >= 1): workgroups walk runs of 64-row query tiles.
+// Persistent banded attention (bf16, D = 128, 4 query heads per KV head):
+// workgroups walk runs of 64-row query tiles. Row r sits at position
+// pos_off + r and sees keys [max(0, pos - W + 1), pos]; W <= 0 means every
+// key up to pos (pos_off + nrows <= cap < 2^31).
 hipError_t launch_band_persist(const void *q, const float *alpha,
                                const float *beta, const void *k_cache,
                                const void *v_cache, void *o, int B, int nrows,
-                               int Hq, int64_t cap, int W,
+                               int pos_off, int Hq, int64_t cap, int W,
                                const HeadGroups &groups, int n_kv,
                                hipStream_t stream);
 

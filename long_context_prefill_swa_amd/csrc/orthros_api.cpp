@@ -276,7 +276,7 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
              groups.gsize == 4) {
     // larger windows (up to the whole prefix): resident workgroups walk
     // runs of query tiles (persistent kernel)
-    e = launch_band_persist(q_pre, alpha, beta, k_cache, v_cache, o, B, T,
+    e = launch_band_persist(q_pre, alpha, beta, k_cache, v_cache, o, B, T, 0,
                             Hq, cap, W, groups, Hkv, as_stream(stream));
   } else if (mfma_eligible(dtype, D, T,
                            {q_pre, alpha, beta, k_cache, v_cache, o})) {
@@ -347,6 +347,12 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
     e = device_flag_ptr(&a.flag);
     if (e != hipSuccess) return hip_fail("device flag", e);
     e = launch_splitkv(a, groups, as_stream(stream));
+  } else if (mfma && groups.gsize == 4) {
+    // many output rows, 4 query heads per KV head: the persistent kernel
+    // with every key up to each row's position
+    e = launch_band_persist(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, B,
+                            T_out, T_in, Hq, cap, 0, groups, Hkv,
+                            as_stream(stream));
   } else if (mfma) {
     e = launch_band_mfma(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, B,
                          T_out, Hq, cap, T_in, 0, groups, Hkv,

@@ -265,8 +265,11 @@ def test_swa_generic_path_fp32_and_other_head_dims():
     (2, 999, 1, 8, 2, torch.bfloat16),      # split-KV, prefilling
     (1, 3000, 4, 8, 2, torch.bfloat16),     # split-KV, 16 rows
     (3, 100, 2, 4, 4, torch.bfloat16),
-    (2, 400, 100, 8, 2, torch.bfloat16),    # banded kernel, unbounded window
+    (2, 400, 100, 8, 2, torch.bfloat16),    # persistent kernel, every key
     (1, 0, 150, 8, 2, torch.bfloat16),      # pre-training setting T_in = 0
+    (1, 777, 333, 8, 2, torch.bfloat16),    # ragged T_in and T_out
+    (2, 64, 1000, 32, 8, torch.bfloat16),   # eight groups, T_out > T_in
+    (1, 200, 64, 16, 2, torch.bfloat16),    # 8 query heads per KV head: banded kernel
     (2, 300, 5, 4, 2, torch.float32),       # generic kernel
 ])
 def test_global_xattn_parity(B, T_in, T_out, Hq, Hkv, dt):
