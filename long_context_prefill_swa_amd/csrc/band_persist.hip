@@ -48,17 +48,12 @@ struct Tiles {
   uint16_t v[2][kBN][kVS];
 };
 struct Smem {
-  union {
-    Tiles t;
-    uint16_t ob[kItemRows][kQS];   // output block (the tiles are free then)
-  };
+  Tiles t;
   float ab[kGs][2][D];             // alpha, beta of the group's heads
 };
-static_assert(sizeof(uint16_t) * kItemRows * kQS <= sizeof(Tiles),
-              "output block fits over the K/V tiles");
-// The next item's query block: a separate LDS object, so that the direct
-// loads into it are not taken to alias the K/V tiles (no conservative waits
-// before the tile reads).
+// The next item's query block, and at the item's end its output block: a
+// separate LDS object, so that the direct loads into it are not taken to
+// alias the K/V tiles (no conservative waits before the tile reads).
 struct QBlock {
   uint16_t qb[kItemRows][kQS];
 };
@@ -181,7 +176,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     uint4 val[kItemRows / kNW];
 #pragma unroll
     for (int rr = 0; rr < kItemRows / kNW; ++rr)
-      val[rr] = *(const uint4 *)&sm.ob[(kItemRows / kNW) * w + rr][8 * ln];
+      val[rr] = *(const uint4 *)&qsm.qb[(kItemRows / kNW) * w + rr][8 * ln];
 #pragma unroll
     for (int rr = 0; rr < kItemRows / kNW; ++rr) {
       const int row = (kItemRows / kNW) * w + rr;
@@ -223,12 +218,16 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   struct Stage {
     uint4 k[kChunks], v[kChunks];
   };
-  auto load_tile = [&](const Item &it, Stage &r, int kt) __attribute__((always_inline)) {
+  // (fresh: the lane's offsets rebuilt here, for the loads between items,
+  // so that they are not kept or spilled across the tile loop)
+  auto load_tile = [&](const Item &it, Stage &r, int kt, bool fresh = false)
+      __attribute__((always_inline)) {
     const uint32_t k_off = (uint32_t)((it.kt0 + kt) * kBN) * (D * 2);
     const uint32_t v_off = k_off - (uint32_t)(kBN * D * 2);
+    const int t_id = fresh ? 64 * w + fresh_lane() : tid;
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const uint32_t off = 16u * (uint32_t)(tid + kNT * i);
+      const uint32_t off = 16u * (uint32_t)(t_id + kNT * i);
       r.k[i] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(it.rk, k_off + off, 0, 0));
       if (kt > 0)
@@ -260,20 +259,9 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   const float qs = kLog2e * rsqrtf((float)D);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // Prologue: the first item's query block.
-  load_qblock(seg);
-  wait_all_vm();
-  __syncthreads();  // query block, alpha / beta
-
-  Item cur = item_of(0);
-  Stage ra, rb;
-  load_tile(cur, rb, 0);
-  load_tile(cur, ra, 1);
-
-  for (int n = 0; n <= n_last; ++n) {
-    // ---- query operand from the block in LDS (B of S^T) --------------------
-    bf16x8 qop[8];
-    {
+  // ---- query operand from the block in LDS (B of S^T) ----------------------
+  bf16x8 qop[8];
+  auto make_qop = [&]() __attribute__((always_inline)) {
       const int ln = fresh_lane();
       const uint16_t *qrow = &qsm.qb[kRows * ps + (ln & 31)][hs * D];
       const float *al = sm.ab[hs][0];
@@ -290,11 +278,24 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
           qop[c][e] = (__bf16)((al[d0 + e] * qv + be[d0 + e]) * qs);
         }
       }
-    }
+  };
+
+  // Prologue: the first item's query block and operand.
+  load_qblock(seg);
+  wait_all_vm();
+  __syncthreads();  // query block, alpha / beta
+  make_qop();
+
+  Item cur = item_of(0);
+  Stage ra, rb;
+  load_tile(cur, rb, 0);
+  load_tile(cur, ra, 1);
+
+  for (int n = 0; n <= n_last; ++n) {
     const int64_t kt0 = cur.kt0;
     const int ntiles = cur.ntiles;
     const int wpos_lo = cur.wpos_lo, wpos_hi = cur.wpos_hi;
-    const int tq = wpos_lo + j;  // this lane's query position
+    const int tq = wpos_lo + (fresh_lane() & 31);  // this lane's position
 
     float m = -INFINITY, l = 0.0f;
     f32x16 acc[4], negm;
@@ -362,8 +363,8 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     store_k(rb, 0);
     store_k(ra, 1);
     store_v(ra, 0);
-    load_tile(cur, ra, 2);
-    __syncthreads();  // tiles in LDS; every wave has read the query block
+    load_tile(cur, ra, 2, true);
+    __syncthreads();  // tiles in LDS; the last item's output block read
     // The next item's query block: issued at the start of the second loop
     // iteration when there is one (its address work then overlaps the
     // step's MFMAs, and it is older than that step's tile loads, whose wait
@@ -377,9 +378,10 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
 
     // Software pipeline, one 64-key tile per step (the banded kernel's).
     auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], Stage &r_in,
-                    Stage &r_out, int it) __attribute__((always_inline)) {
+                    Stage &r_out, int it, bool fresh = false)
+        __attribute__((always_inline)) {
       const int64_t kb = (kt0 + it) * kBN;
-      load_tile(cur, r_out, it + 3);  // stored at the end of the next step
+      load_tile(cur, r_out, it + 3, fresh);  // stored at the end of the next step
       scores(sn, (it + 1) & 1);
       bf16x8 pop[4];
 #pragma unroll
@@ -424,6 +426,10 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
       settle(sn, kb + kBN);
       store_k(r_in, it & 1);     // K of tile it+2
       store_v(r_in, vb ^ 1);     // V of tile it+1
+      // All but this step's four tile loads are complete (the counter
+      // retires in order): in particular the next item's query block, if it
+      // was issued before them, so that after this barrier it is visible.
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
       __syncthreads();
     };
     int it = 0;
@@ -433,20 +439,22 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
       step(sa, sb, ra, rb, it);
       step(sb, sa, rb, ra, it + 1);
     }
-    if (it < ntiles) step(sa, sb, ra, rb, it);
+    if (it < ntiles) step(sa, sb, ra, rb, it, true);
 
     // ---- item end ----------------------------------------------------------
-    // Every load so far is complete after this wait (the tile run-out and the
-    // next query block); the next item's first tiles are requested at once.
-    wait_all_vm();
+    // The next query block is complete and visible (issued before a step
+    // whose wait covers it, and that step's barrier). Request the next
+    // item's first tiles, take its query operand, then normalise this
+    // item's rows into the query block over the slots this wave has just
+    // read (no other wave reads them) and write the block out as whole
+    // rows.
     const int qt = cur.qt;
     if (n < n_last) {
       cur = item_of(n + 1);
-      load_tile(cur, rb, 0);
-      load_tile(cur, ra, 1);
+      load_tile(cur, rb, 0, true);
+      load_tile(cur, ra, 1, true);
+      make_qop();
     }
-    // Normalise this wave's rows into the output block over the K/V tiles
-    // (free after the last step's barrier) and write it out as whole rows.
     {
       // row sum: this lane's half plus its partner's (lane ^ 32)
       const auto lp = __builtin_amdgcn_permlane32_swap(
@@ -454,7 +462,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
       const float inv =
           1.0f / (__uint_as_float(lp[0]) + __uint_as_float(lp[1]));
       const int ln = fresh_lane();
-      uint16_t *orow = &sm.ob[kRows * ps + (ln & 31)][hs * D];
+      uint16_t *orow = &qsm.qb[kRows * ps + (ln & 31)][hs * D];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -472,9 +480,8 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
           *(uint2 *)(orow + d0) = make_uint2(pk[0], pk[1]);
         }
     }
-    __syncthreads();  // output block complete; the next query block visible
+    __syncthreads();  // output block complete
     store_oblock(qt);
-    __syncthreads();  // output block read before the tiles are refilled
   }
 }
 
