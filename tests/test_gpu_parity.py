@@ -236,6 +236,40 @@ def test_swa_persistent_padded_group():
             dt, "swa")
 
 
+@pytest.mark.parametrize("T", [1, 2, 63, 65])
+@pytest.mark.parametrize("Hq,Hkv,W", [
+    (8, 2, 1),      # rolling kernel, window of one
+    (8, 2, 100),    # rolling kernel
+    (8, 2, 300),    # persistent kernel
+    (16, 2, 300),   # banded kernel (8 query heads per KV head)
+])
+def test_swa_short_sequences(T, Hq, Hkv, W):
+    """Sequences shorter than, equal to and one past a 64-row tile."""
+    B, D = 2, 128
+    say(f"[swa short] T={T} Hq={Hq} Hkv={Hkv} W={W}")
+    dt = torch.bfloat16
+    q, k, v = rand((B, T, Hq, D), 60, dt), rand((B, T, Hkv, D), 61, dt), rand((B, T, Hkv, D), 62, dt)
+    a, b = affine_pair(Hq * D, 63)
+    o = run_swa(q, a, b, k, v, W)
+    compare(o, oracle_swa(q, a, b, k, v, W), dt, "swa")
+
+
+def test_global_single_row_at_position_zero():
+    """T_in = 0, T_out = 1: the one output row sees only key 0."""
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    dt = torch.bfloat16
+    say("[global single row]")
+    qx = rand((B, 1, Hq, D), 64, dt)
+    k, v = rand((B, 1, Hkv, D), 65, dt), rand((B, 1, Hkv, D), 66, dt)
+    a, b = affine_pair(Hq * D, 67)
+    kc, vc, _ = make_cache(k, v, 40, fill=float("nan"))
+    ox = torch.empty_like(qx)
+    lo.orthros_global_xattn(qx, a, b, kc, vc, ox, 0)
+    torch.cuda.synchronize()
+    ref = oracle.xattn(f64(qx), f64(a), f64(b), f64(k), f64(v), 0)[0]
+    compare(ox, ref, dt, "global")
+
+
 @pytest.mark.parametrize("hmap", [[2, 0, 1, 1, 0, 2], [0, 0, 0, 1, 2, 2]])
 def test_swa_custom_head_map(hmap):
     B, T, D, Hkv = 2, 200, 128, 3
