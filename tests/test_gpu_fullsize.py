@@ -160,3 +160,66 @@ def test_long_prefill_trained_window_sampled():
     ts = sample_rows(cfg.T, 128, 24, cfg_id + 7)
     check_rows(o, x.q_pre, x.alpha, x.beta, k_host, v_host, ts, 128,
                "base stream W=128")
+
+
+def test_largest_cache_length():
+    """The largest cache the MFMA paths accept: T = 2^24 - 1 keys, whose
+    byte offsets within one (sequence, KV head) slab just fit the 32-bit
+    buffer offsets. One KV head with four query heads (about 47 GB on the
+    GPU). Checked: sampled base-stream rows at W = 4096 (persistent kernel)
+    and at W = 128 (rolling kernel), and the output-stream row at the last
+    position over all 2^24 - 1 keys. Its reference is the oracle evaluated
+    over 16 key slices, each with every key visible, whose results are
+    combined by their log-sum-exp weights (exact: o = sum_c
+    exp(lse_c - L) o_c with L = log sum_c exp(lse_c))."""
+    B, Hq, Hkv, D = 1, 4, 1, 128
+    T = (1 << 24) - 1
+    dt = torch.bfloat16
+    say(f"[full size] largest cache: T={T} Hq={Hq} Hkv={Hkv}")
+    from workloads import normal
+    q = normal((B, T, Hq, D), 9101, dt, DEV)
+    k = normal((B, T, Hkv, D), 9102, dt, DEV)
+    v = normal((B, T, Hkv, D), 9103, dt, DEV)
+    qx = normal((B, 1, Hq, D), 9104, dt, DEV)
+    a = 1 + 0.1 * normal((Hq * D,), 9105, torch.float32, DEV)
+    b = 0.1 * normal((Hq * D,), 9106, torch.float32, DEV)
+    kc = torch.empty((B, Hkv, T, D), dtype=dt, device=DEV)
+    vc = torch.empty_like(kc)
+    cl = torch.zeros(B, dtype=torch.int32, device=DEV)
+    lo.orthros_kv_append(kc, vc, cl, k, v)
+    o = torch.empty_like(q)
+    ox = torch.empty_like(qx)
+    lo.orthros_global_xattn(qx, a, b, kc, vc, ox, T - 1)
+    torch.cuda.synchronize()
+    assert cl.tolist() == [T]
+    ts = [0, 1, 4095, 4096, (1 << 23) - 1, 1 << 23, T - 65, T - 64, T - 2,
+          T - 1]
+    for W in (4096, 128):
+        lo.orthros_swa_prefill(q, a, b, kc, vc, o, W)
+        torch.cuda.synchronize()
+        got, ref = [], []
+        for t in ts:
+            lo_t = max(0, t - W + 1)
+            r, _ = oracle.xattn(f64(q[:, t:t + 1]), f64(a), f64(b),
+                                f64(k[:, lo_t:t + 1]), f64(v[:, lo_t:t + 1]),
+                                t - lo_t)
+            ref.append(r)
+            got.append(f64(o[:, t:t + 1]))
+        compare(np.concatenate(got, 1), np.concatenate(ref, 1), dt,
+                f"base stream W={W} ({len(ts)} rows)")
+    del o
+    torch.cuda.empty_cache()
+    # output stream over every key, as 16 slices merged by log-sum-exp
+    n_sl = 16
+    bounds = [T * i // n_sl for i in range(n_sl + 1)]
+    outs, lses = [], []
+    for s0, s1 in zip(bounds[:-1], bounds[1:]):
+        r, l = oracle.xattn(f64(qx), f64(a), f64(b), f64(k[:, s0:s1]),
+                            f64(v[:, s0:s1]), s1 - s0 - 1)
+        outs.append(r)     # [B, 1, Hq, D]
+        lses.append(l)     # [B, 1, Hq]
+    lse = np.stack(lses)                       # [n_sl, B, 1, Hq]
+    L = lse.max(0) + np.log(np.exp(lse - lse.max(0)).sum(0))
+    wts = np.exp(lse - L)[..., None]           # [n_sl, B, 1, Hq, 1]
+    ref = (wts * np.stack(outs)).sum(0)
+    compare(ox, ref, dt, f"output row over {T} keys")
