@@ -292,12 +292,17 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   load_tile(cur, ra, 1);
 
   for (int n = 0; n <= n_last; ++n) {
-    const int64_t kt0 = cur.kt0;
+    const int kt0 = cur.kt0;
     const int ntiles = cur.ntiles;
     const int wpos_lo = cur.wpos_lo, wpos_hi = cur.wpos_hi;
     const int tq = wpos_lo + (fresh_lane() & 31);  // this lane's position
 
-    float m = -INFINITY, l = 0.0f;
+    float m = -INFINITY;
+    // the lazy-rescale threshold on the tile maximum (relative to m):
+    // -inf while this row has seen no key, then kTau
+    float thr = -INFINITY;
+    // row-sum partials, one per 16-key group: four short dependency chains
+    float l4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     f32x16 acc[4], negm;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -321,8 +326,9 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
         }
     };
     // Band mask (only tiles crossing a band edge of some row of this wave),
-    // row maximum, and the lazy move of the reference maximum.
-    auto settle = [&](f32x16 (&sn)[2], int64_t kb) __attribute__((always_inline)) {
+    // row maximum, and the lazy move of the reference maximum. The tile
+    // offset is a 32-bit uniform value, so the band test is scalar.
+    auto settle = [&](f32x16 (&sn)[2], int kb) __attribute__((always_inline)) {
       const bool inside = kb >= wpos_hi - W + 1 && kb + kBN - 1 <= wpos_lo;
       if (!inside) {
         const int d0 = (int)(kb - tq);
@@ -334,25 +340,32 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
             sn[sk][v] = (d > 0 || d <= -W) ? -INFINITY : sn[sk][v];
           }
       }
-      float tmax = -INFINITY;
+      // four independent chains over this lane's 32 scores
+      float t4[4];
 #pragma unroll
-      for (int sk = 0; sk < 2; ++sk)
+      for (int c = 0; c < 4; ++c) {
+        t4[c] = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sn[sk][v]);
+        for (int v = 0; v < 8; ++v)
+          t4[c] = fmaxf(t4[c], sn[c >> 1][8 * (c & 1) + v]);
+      }
+      float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
       tmax = max_xor32(tmax);
-      const bool need = (m == -INFINITY) ? (tmax > -INFINITY) : (tmax > kTau);
+      const bool need = tmax > thr;
       if (__any(need)) {
         const float shift = need ? tmax : 0.0f;
         const float corr =
             need ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(-shift))
                  : 1.0f;
         m = need ? ((m == -INFINITY) ? shift : m + shift) : m;
-        l *= corr;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) l4[c] *= corr;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
 #pragma unroll
         for (int sk = 0; sk < 2; ++sk) sn[sk] -= shift;
         const float nm = (m == -INFINITY) ? 0.0f : -m;
+        thr = (m == -INFINITY) ? -INFINITY : kTau;
 #pragma unroll
         for (int v = 0; v < 16; ++v) negm[v] = nm;
       }
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], Stage &r_in,
                     Stage &r_out, int it, bool fresh = false)
         __attribute__((always_inline)) {
-      const int64_t kb = (kt0 + it) * kBN;
+      const int kb = (kt0 + it) * kBN;
       load_tile(cur, r_out, it + 3, fresh);  // stored at the end of the next step
       scores(sn, (it + 1) & 1);
       bf16x8 pop[4];
@@ -390,10 +403,15 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
         for (int e = 0; e < 8; ++e)
           pop[kg][e] =
               (__bf16)__builtin_amdgcn_exp2f(sc[kg >> 1][8 * (kg & 1) + e]);
+        // row sum of the same bf16 probabilities, from the packed operand
+        // words (through scalars: a bit cast of a vector element reads
+        // element 0)
+        const u32x4 pw = __builtin_bit_cast(u32x4, pop[kg]);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pop[kg][e], pop[kg][e + 1]};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w2 = pw[e];
+          l4[kg] = __builtin_amdgcn_fdot2_f32_bf16(
+              __builtin_bit_cast(bf16x2, w2), ones, l4[kg], false);
         }
       }
       const int vb = it & 1;
@@ -456,6 +474,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
       make_qop();
     }
     {
+      const float l = (l4[0] + l4[1]) + (l4[2] + l4[3]);
       // row sum: this lane's half plus its partner's (lane ^ 32)
       const auto lp = __builtin_amdgcn_permlane32_swap(
           __float_as_uint(l), __float_as_uint(l), false, false);
