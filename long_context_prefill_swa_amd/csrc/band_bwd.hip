@@ -79,6 +79,22 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
+// Block -> (unit, (batch, head group) pair). Workgroups are dealt to the
+// 8 XCDs by block id; when the pairs are a multiple of 8, pair p's units
+// (row tiles or key blocks) all run on XCD p % 8, so the rows they share
+// (K/V bands, Q/dO blocks) are re-read from that XCD's L2, not from HBM.
+__device__ __forceinline__ void xcd_unit(int n_units, int &unit, int &pair) {
+  const int n_pairs = (int)(gridDim.x / (unsigned)n_units);
+  if (n_pairs % 8 == 0) {
+    const int xcd = (int)(blockIdx.x % 8u), slot = (int)(blockIdx.x / 8u);
+    unit = slot % n_units;
+    pair = xcd + 8 * (slot / n_units);
+  } else {
+    unit = (int)(blockIdx.x % (unsigned)n_units);
+    pair = (int)(blockIdx.x / (unsigned)n_units);
+  }
+}
+
 // First key of row position p's range (W >= p + 1 means the whole prefix).
 __device__ __forceinline__ int range_lo(int p, int W) {
   return p >= W ? p - W + 1 : 0;
@@ -100,8 +116,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
   constexpr int kRowsWg = 32 * (8 / GS);
   __shared__ __attribute__((aligned(16))) DqSmem<GS> sm;
   const int n_wg_rows = (a.nrows + kRowsWg - 1) / kRowsWg;
-  const int wr = blockIdx.x % n_wg_rows;
-  const int rest = blockIdx.x / n_wg_rows;
+  int wr, rest;
+  xcd_unit(n_wg_rows, wr, rest);
   const int gi = rest % groups.n_groups;
   const int b = rest / groups.n_groups;
 
@@ -435,8 +451,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     BwdKvArgs a, HeadGroups groups) {
   __shared__ __attribute__((aligned(16))) DkvSmem<GS> sm;
   const int n_kt = (a.T + kKvKeys - 1) / kKvKeys;
-  const int kt = blockIdx.x % n_kt;
-  const int rest = blockIdx.x / n_kt;
+  int kt, rest;
+  xcd_unit(n_kt, kt, rest);
   const int gi = rest % groups.n_groups;  // the one group of this KV head
   const int b = rest / groups.n_groups;
   const int kvh = groups.kv[gi];
