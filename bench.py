@@ -80,6 +80,74 @@ def traffic_from_profile(name, sha):
     return float(m_b.group(1))
 
 
+def stats(xs):
+    """mean, median, p10, p90 and count of a list of times (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)),
+            "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def shader_clock(dev, iters=100000):
+    """Average shader clock (MHz) while every compute unit runs MFMA chains
+    (libclock_probe.so: shader-cycle counter over the constant-rate wall
+    counter), or None if the probe is not built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "long_context_prefill_swa_amd",
+                        "libclock_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                              ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    L.clock_probe.restype = ctypes.c_int
+    n_blocks = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.zeros(3 * n_blocks, dtype=torch.int64, device=dev)
+    khz = ctypes.c_int(0)
+    stream = torch.cuda.current_stream(dev)
+    rc = L.clock_probe(ctypes.c_void_p(out.data_ptr()), n_blocks, iters,
+                       ctypes.byref(khz),
+                       ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"clock probe failed: hip error {rc}")
+    torch.cuda.synchronize()
+    r = out.view(n_blocks, 3).cpu().double()
+    cycles, ticks = r[:, 0].sum().item(), r[:, 1].sum().item()
+    return cycles / (ticks / (khz.value * 1e3)) / 1e6
+
+
+def run_context(dev, clock_before, clock_after):
+    import torch
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    rocm = ""
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    p = torch.cuda.get_device_properties(dev)
+    return {"gpu": p.name, "gcn_arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count,
+            "shader_clock_mhz_under_mfma_load":
+                {"before": clock_before, "after": clock_after},
+            "rocm": rocm, "torch": torch.__version__,
+            "torch_hip": torch.version.hip, "cpu_model": cpu,
+            "cpu_count": os.cpu_count(),
+            "cpu_affinity": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +221,15 @@ def main():
         e.record(stream)
         return e
 
+    # The 256 MB Infinity Cache (MALL) would serve part of a memory-bound
+    # pass from the previous launch's reads. Reading 1 GiB of other data
+    # evicts it (and the L2s). A read, not a write: a written buffer would
+    # leave dirty lines whose write-back the next pass would pay for.
+    flush_buf = torch.zeros((1 << 30) // 4, dtype=torch.float32, device=dev)
+
+    def mall_flush():
+        flush_buf.sum()
+
     def step(record):
         marks = {}
         if run_prefill:
@@ -163,21 +240,33 @@ def main():
             lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4,
                                    pc.W)
             marks["p2"] = ev()
+            # output row right after the window pass, as a prefill runs it
+            # (K/V partly still in the MALL): the warm figure
             lo.orthros_global_xattn(px.qx_pre, px.alpha_x, px.beta_x, kc4,
                                     vc4, ox4, pc.T_in, ws=ws4)
             marks["p3"] = ev()
+            mall_flush()
+            marks["p4"] = ev()
+            # the same call from HBM: the reported figure
+            lo.orthros_global_xattn(px.qx_pre, px.alpha_x, px.beta_x, kc4,
+                                    vc4, ox4, pc.T_in, ws=ws4)
+            marks["p5"] = ev()
         if run_decode:
             cl3.fill_(dc.T)
-            marks["d0"] = ev()
+            mall_flush()
+            dm = [ev()]
             for s in range(n_dec):
                 lo.orthros_decode_pair(st.q_pre[s], st.qx_pre[s], a3, b3, ax3,
                                        bx3, st.k_new[s], st.v_new[s], kc3,
                                        vc3, cl3, o3, ox3, dc.T + s + 1, dc.W,
                                        ws=ws3)
-            marks["d1"] = ev()
+                dm.append(ev())
+            marks["d"] = dm
         if record is not None:
             record.append(marks)
 
+    clock_before = shader_clock(dev)
+    log(f"[bench] shader clock under MFMA load: {clock_before:.0f} MHz")
     log(f"[bench] warmup {args.warmup} step(s)")
     for _ in range(args.warmup):
         step(None)
@@ -198,9 +287,10 @@ def main():
     lo.orthros_check_device_errors()
     if run_decode:
         assert cl3.tolist() == [dc.T + n_dec] * dc.B, "decode cache lengths"
+    clock_after = shader_clock(dev)
 
-    def avg(a, b):
-        return sum(r[a].elapsed_time(r[b]) for r in recs) / len(recs)
+    def leg(a, b):
+        return stats([r[a].elapsed_time(r[b]) for r in recs])
 
     out = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup,
@@ -211,10 +301,13 @@ def main():
                       "prefill_128k": "B=1 Hq=32 Hkv=8 D=128 T=131072 W=4096 T_out=1",
                       "decode_pair_b64": "B=64 Hq=32 Hkv=8 D=128 L0=32768 W=2048 steps=256",
                       "global_batch": pc.B, "seq_len": pc.T}}
+    out["run"] = run_context(dev, clock_before, clock_after)
     log(f"[bench] wall {wall:.2f}s, events {total_ms:.1f} ms")
 
     if run_prefill:
-        t_app, t_swa, t_glob = avg("p0", "p1"), avg("p1", "p2"), avg("p2", "p3")
+        s_app, s_swa = leg("p0", "p1"), leg("p1", "p2")
+        s_glob_warm, s_glob = leg("p2", "p3"), leg("p4", "p5")
+        t_app, t_swa, t_glob = s_app["mean"], s_swa["mean"], s_glob["mean"]
         t_pre = t_app + t_swa + t_glob
         F_swa = 4.0 * pc.D * band_pairs(pc.T, pc.W) * pc.Hq * pc.B
         F_glob = 4.0 * pc.D * pc.T * pc.Hq * pc.B
@@ -224,14 +317,21 @@ def main():
         out["prefill"] = {
             "ms_kv_append": t_app, "ms_swa": t_swa, "ms_global": t_glob,
             "ms_total": t_pre,
+            "timing": {"kv_append": s_app, "swa": s_swa,
+                       "global_from_hbm": s_glob,
+                       "global_warm_after_swa": s_glob_warm},
             "attention_tflops": (F_swa + F_glob) / ((t_swa + t_glob) * 1e-3) / 1e12,
             "attention_frac_of_bf16_peak":
                 (F_swa + F_glob) / ((t_swa + t_glob) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "swa_tflops": swa_tflops,
+            "swa_tflops_median": F_swa / (s_swa["median"] * 1e-3) / 1e12,
             "global_GBps": kv_bytes / (t_glob * 1e-3) / 1e9,
             "global_frac_of_hbm_peak": kv_bytes / (t_glob * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "global_warm_GBps": kv_bytes / (s_glob_warm["mean"] * 1e-3) / 1e9,
             "kv_append_GBps": 2 * kv_bytes / (t_app * 1e-3) / 1e9,
-        }
+            "notes": "global_from_hbm follows a 1 GiB write that evicts the "
+                     "MALL; global_warm_after_swa directly follows the "
+                     "window pass (extra). value uses the HBM figure."}
         sha = kernel_sha(BAND_SRC)
         out["roofline"] = {
             "kernel": "band_persist_kernel (sliding-window prefill, prefill_128k)",
@@ -240,11 +340,24 @@ def main():
             "traffic": traffic_from_profile("band_persist_prefill_128k", sha),
             "algorithmic_flop_per_launch": F_swa,
             "avg_launch_ms": t_swa, "kernel_source_sha256": sha}
+        sha_g = kernel_sha(SPLIT_SRC)
+        out["roofline_global"] = {
+            "kernel": "split-KV output row (prefill_128k, 131072 keys), from HBM",
+            "bound": "hbm", "achieved": kv_bytes / (t_glob * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": kv_bytes / (t_glob * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "traffic": traffic_from_profile("splitkv_global_128k", sha_g),
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "avg_launch_ms": t_glob, "kernel_source_sha256": sha_g}
         log(f"[bench] prefill: append {t_app:.3f} ms, swa {t_swa:.3f} ms "
-            f"({swa_tflops:.1f} TFLOP/s), global {t_glob:.3f} ms")
+            f"({swa_tflops:.1f} TFLOP/s), global {t_glob:.3f} ms from HBM, "
+            f"{s_glob_warm['mean']:.3f} ms warm")
 
     if run_decode:
-        t_dec = avg("d0", "d1")
+        passes = [r["d"][0].elapsed_time(r["d"][-1]) for r in recs]
+        per_step = [r["d"][i].elapsed_time(r["d"][i + 1])
+                    for r in recs for i in range(n_dec)]
+        t_dec = sum(passes) / len(passes)
         # algorithmic bytes per step: every cached K/V row read once per
         # (sequence, KV head), plus the appended row, queries and outputs
         L_sum = sum(dc.T + s + 1 for s in range(n_dec))
@@ -253,8 +366,12 @@ def main():
         gbps = (kv_read + small) / (t_dec * 1e-3) / 1e9
         out["decode_pair"] = {
             "ms_per_step": t_dec / n_dec, "ms_256_steps": t_dec,
+            "step_latency_ms": stats(per_step),
+            "pass_ms": stats(passes),
             "kv_GBps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS,
-            "algorithmic_bytes_256_steps": kv_read + small}
+            "algorithmic_bytes_256_steps": kv_read + small,
+            "notes": "each 256-step pass follows a 1 GiB write that evicts "
+                     "the MALL"}
         # The decode pair's dominant kernel is the split-KV stream; its
         # launch is bracketed together with the short merge kernel.
         sha_s = kernel_sha(SPLIT_SRC)
@@ -272,37 +389,46 @@ def main():
 
     # ---- full causal attention at the same T (speedup ratio) --------------
     if run_prefill and not args.no_causal:
-        reps = 2
+        reps = 5
         lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4, pc.T)
         torch.cuda.synchronize()
-        e0 = ev()
+        evs = [ev()]
         for _ in range(reps):
             lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4,
                                    pc.T)
-        e1 = ev()
+            evs.append(ev())
         torch.cuda.synchronize()
-        t_c = e0.elapsed_time(e1) / reps
+        sc = stats([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)])
+        t_c = sc["mean"]
         F_c = 4.0 * pc.D * causal_pairs(pc.T) * pc.Hq * pc.B
-        out["causal"] = {"ms": t_c, "tflops": F_c / (t_c * 1e-3) / 1e12,
-                         "speedup_vs_swa": t_c / out["prefill"]["ms_swa"]}
+        out["causal"] = {"ms": t_c, "timing": sc,
+                         "tflops": F_c / (t_c * 1e-3) / 1e12,
+                         "speedup_vs_swa": t_c / out["prefill"]["ms_swa"],
+                         "speedup_vs_swa_median":
+                             sc["median"] / out["prefill"]["timing"]["swa"]["median"]}
         log(f"[bench] causal {t_c:.2f} ms, speedup {t_c / out['prefill']['ms_swa']:.1f}x")
 
     # ---- the window the paper trains with (W = 128) at the same T ----------
     if run_prefill:
-        reps, W_s = 3, 128
+        reps, W_s = 20, 128
         lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4, W_s)
         torch.cuda.synchronize()
-        e0 = ev()
+        ts_ = []
         for _ in range(reps):
+            mall_flush()
+            e0 = ev()
             lo.orthros_swa_prefill(px.q_pre, px.alpha, px.beta, kc4, vc4, o4,
                                    W_s)
-        e1 = ev()
+            e1 = ev()
+            ts_.append((e0, e1))
         torch.cuda.synchronize()
-        t_s = e0.elapsed_time(e1) / reps
+        s_w = stats([a.elapsed_time(b) for a, b in ts_])
+        t_s = s_w["mean"]
         # every byte of Q, O, K and V crosses HBM once
         by = 2 * 2 * pc.B * pc.T * pc.D * (pc.Hq + pc.Hkv)
         out["swa_w128"] = {
-            "ms": t_s, "tokens_per_s": pc.B * pc.T / (t_s * 1e-3),
+            "ms": t_s, "timing": s_w, "notes": "each launch follows a MALL flush",
+            "tokens_per_s": pc.B * pc.T / (t_s * 1e-3),
             "tflops": 4.0 * pc.D * band_pairs(pc.T, W_s) * pc.Hq * pc.B
             / (t_s * 1e-3) / 1e12,
             "algorithmic_bytes": by, "gbps": by / (t_s * 1e-3) / 1e9,
@@ -326,7 +452,7 @@ def main():
     # ---- the other prefill shapes: 32K single layer, SFT dual stream -------
     if run_prefill and not args.no_other_prefills:
         out["other_prefills"] = {
-            name: prefill_leg(lo, name, dev, ev)
+            name: prefill_leg(lo, name, dev, ev, mall_flush)
             for name in ("prefill_32k", "sft_dual_8k")}
 
     # ---- training backward at the SFT shape (both streams) ------------------
@@ -338,7 +464,7 @@ def main():
         del kc3, vc3
         torch.cuda.empty_cache()
         out["decode_pair_paged_ragged"] = paged_ragged_decode(
-            lo, dc, dc_id, st, a3, b3, ax3, bx3, dev, ev)
+            lo, dc, dc_id, st, a3, b3, ax3, bx3, dev, ev, mall_flush)
 
     # ---- CPU oracle on a bounded sample --------------------------------------
     if run_prefill and not args.no_cpu_baseline:
@@ -347,7 +473,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def backward_leg(lo, dev, ev, reps=2):
+def backward_leg(lo, dev, ev, reps=5):
     """orthros_attn_backward at the SFT dual-stream shape (B=4, T=8192,
     T_out=2048, W=1024, 32/8 heads): forward outputs from the library, unit
     upstream gradients. Algorithmic FLOPs: 8 D per (row, key) pair of either
@@ -378,15 +504,17 @@ def backward_leg(lo, dev, ev, reps=2):
                                         d_o, d_ox, c.W, out=g, ws=ws)
     g = f()
     torch.cuda.synchronize()
-    e0 = ev()
+    evs = [ev()]
     for _ in range(reps):
         f()
-    e1 = ev()
+        evs.append(ev())
     torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / reps
+    sb = stats([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)])
+    t = sb["mean"]
     pairs = band_pairs(c.T, c.W) + sum(c.T_in + r + 1 for r in range(c.T_out))
     flop = 8.0 * c.D * pairs * c.Hq * c.B
-    res = {"workload": c.name, "ms": t, "tflops": flop / (t * 1e-3) / 1e12,
+    res = {"workload": c.name, "ms": t, "timing": sb,
+           "tflops": flop / (t * 1e-3) / 1e12,
            "algorithmic_tflop": flop / 1e12,
            "mfma_frac": flop / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
     log(f"[bench] backward {c.name}: {t:.2f} ms, {res['tflops']:.0f} TFLOP/s")
@@ -402,7 +530,7 @@ def global_pairs(T, T_out):
     return T_out * T_in + T_out * (T_out + 1) // 2
 
 
-def prefill_leg(lo, name, dev, ev, reps=5):
+def prefill_leg(lo, name, dev, ev, flush, reps=20):
     """One prefill of workload `name` (cache fill, sliding window, output
     stream), its attention TFLOP/s and tokens/s."""
     import torch
@@ -424,6 +552,9 @@ def prefill_leg(lo, name, dev, ev, reps=5):
         marks.append(ev())
         lo.orthros_swa_prefill(x.q_pre, x.alpha, x.beta, kc, vc, o, c.W)
         marks.append(ev())
+        if c.T_out == 1:
+            flush()      # the one-row pass is memory-bound: from HBM
+        marks.append(ev())
         lo.orthros_global_xattn(x.qx_pre, x.alpha_x, x.beta_x, kc, vc, ox,
                                 c.T_in, ws=ws)
         marks.append(ev())
@@ -435,12 +566,16 @@ def prefill_leg(lo, name, dev, ev, reps=5):
         run(m)
         recs.append(m)
     torch.cuda.synchronize()
-    t = [sum(r[i].elapsed_time(r[i + 1]) for r in recs) / reps for i in range(3)]
+    legs = [stats([r[i].elapsed_time(r[i + 1]) for r in recs])
+            for i in (0, 1, 3)]
+    t = [g["mean"] for g in legs]
     F_swa = 4.0 * c.D * band_pairs(c.T, c.W) * c.Hq * c.B
     F_glob = 4.0 * c.D * global_pairs(c.T, c.T_out) * c.Hq * c.B
     res = {"config": f"B={c.B} Hq={c.Hq} Hkv={c.Hkv} D={c.D} T={c.T} "
                      f"W={c.W} T_out={c.T_out}",
            "ms_kv_append": t[0], "ms_swa": t[1], "ms_global": t[2],
+           "timing": {"kv_append": legs[0], "swa": legs[1],
+                      "global": legs[2]},
            "tokens_per_s": c.B * c.T / (sum(t) * 1e-3),
            "swa_tflops": F_swa / (t[1] * 1e-3) / 1e12,
            "global_tflops": F_glob / (t[2] * 1e-3) / 1e12,
@@ -452,7 +587,7 @@ def prefill_leg(lo, name, dev, ev, reps=5):
     return res
 
 
-def layer_forward_leg(lo, pc, pc_id, kc, vc, dev, ev, reps=2):
+def layer_forward_leg(lo, pc, pc_id, kc, vc, dev, ev, reps=5):
     """One Orthros layer at the 128K prefill shape (d_model = Hq*D = 4096,
     one output row): hipBLASLt projections, cache fill, both attention
     streams and W_O, at the configuration's window and at W = 128."""
@@ -476,13 +611,15 @@ def layer_forward_leg(lo, pc, pc_id, kc, vc, dev, ev, reps=2):
                                      y, pc.T_out, W, ws=ws)
         f()
         torch.cuda.synchronize()
-        e0 = ev()
+        evs = [ev()]
         for _ in range(reps):
             f()
-        e1 = ev()
+            evs.append(ev())
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / reps
-        res[f"W{W}"] = {"ms": t, "tokens_per_s": B * pc.T / (t * 1e-3)}
+        sl = stats([evs[i].elapsed_time(evs[i + 1]) for i in range(reps)])
+        t = sl["mean"]
+        res[f"W{W}"] = {"ms": t, "timing": sl,
+                        "tokens_per_s": B * pc.T / (t * 1e-3)}
         log(f"[bench] layer W={W}: {t:.2f} ms, "
             f"{B * pc.T / (t * 1e-3) / 1e6:.2f} M tokens/s")
     lo.orthros_check_device_errors()
@@ -491,8 +628,8 @@ def layer_forward_leg(lo, pc, pc_id, kc, vc, dev, ev, reps=2):
     return res
 
 
-def paged_ragged_decode(lo, dc, dc_id, st, a, b, ax, bx, dev, ev,
-                        page_size=64, reps=2):
+def paged_ragged_decode(lo, dc, dc_id, st, a, b, ax, bx, dev, ev, flush,
+                        page_size=64, reps=3):
     """256 decode pair steps on a paged cache with ragged lengths: B=64
     sequences of seeded lengths uniform in [16384, 49152] (mean 32768), page
     size 64, pages of each sequence scattered over the pool by a seeded
@@ -536,6 +673,7 @@ def paged_ragged_decode(lo, dc, dc_id, st, a, b, ax, bx, dev, ev,
 
     def run():
         cl.copy_(cl0)
+        flush()
         e0 = ev()
         for s in range(n_dec):
             lo.orthros_decode_pair_paged(
@@ -554,12 +692,13 @@ def paged_ragged_decode(lo, dc, dc_id, st, a, b, ax, bx, dev, ev,
     lo.orthros_check_device_errors()
     assert cl.tolist() == [n + n_dec for n in lens], "paged decode lengths"
     t = sum(times) / len(times)
+    sp = stats(times)
     kv = sum(2.0 * dc.Hkv * dc.D * 2 * sum(n + s + 1 for s in range(n_dec))
              for n in lens)
     small = n_dec * dc.B * (4 * dc.Hq * dc.D * 2 + 2 * dc.Hkv * dc.D * 2)
     gbps = (kv + small) / (t * 1e-3) / 1e9
     log(f"[bench] paged ragged decode: {t / n_dec:.3f} ms/step, {gbps:.0f} GB/s")
-    return {"ms_per_step": t / n_dec, "kv_GBps": gbps,
+    return {"ms_per_step": t / n_dec, "pass_ms": sp, "kv_GBps": gbps,
             "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS, "page_size": page_size,
             "lengths": "B=64 uniform in [16384, 49152], mean "
                        f"{sum(lens) / len(lens):.0f}",

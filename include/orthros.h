@@ -25,8 +25,13 @@
  *    here, so the base range is [max(0, t-W+1), t] (exactly min(t+1, W) keys)
  *    and the output range is [0, t].
  *  * Device pointers (marked [dev]) point to device memory owned by the
- *    caller; the library never allocates or frees device memory and keeps no
- *    pointer after a call returns. Tensors are dense, row-major, no strides.
+ *    caller; the library keeps no pointer after a call returns. The
+ *    attention entry points never allocate or free device memory: scratch
+ *    comes from the caller (ws arguments). Two pieces of device memory are
+ *    the library's own: a sticky error flag per device (a static device
+ *    variable, see orthros_check_device_errors), and the hipBLASLt handle
+ *    that orthros_layer_forward creates on its first call on a device (the
+ *    library's allocation, kept until the process ends). Tensors are dense, row-major, no strides.
  *    Host pointers are marked [host] and are read before the call returns.
  *  * Element type `dtype`: ORTHROS_F32 or ORTHROS_BF16 for Q, K, V and the
  *    outputs. alpha/beta vectors are always fp32 with Hq*D entries (one per
@@ -59,7 +64,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 5
+#define ORTHROS_ABI_VERSION 6
 
 /* dtype codes */
 #define ORTHROS_F32 0
@@ -154,9 +159,9 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
  *   k_cache, v_cache [dev] [B, Hkv, cap, D], cap >= T_in + T_out
  *   o_x          [dev] [B, T_out, Hq, D] dtype, written
  *   ws, ws_bytes [dev] scratch of at least orthros_workspace_bytes(
- *                ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D, T_out, T_in+T_out)
- *                bytes (may be NULL when that size is 0); contents on entry
- *                are ignored and left undefined.
+ *                ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D, T_out, T_in+T_out,
+ *                head_map) bytes (may be NULL when that size is 0); contents
+ *                on entry are ignored and left undefined.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
  */
 int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
@@ -196,7 +201,8 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
  *                      raised.
  *   W                  base window, >= 1
  *   ws, ws_bytes       scratch of orthros_workspace_bytes(
- *                      ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after)
+ *                      ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after,
+ *                      head_map)
  * Errors: EINVAL, EUNSUPPORTED, ECAPACITY (max_len_after > cap), EWORKSPACE,
  * EHIP.
  */
@@ -258,7 +264,8 @@ int orthros_kv_append_paged(void *k_pool, void *v_pool, int64_t n_pages,
  *   max_len_after  host upper bound of cache_len[b] + 1 over all b,
  *                  1 <= max_len_after <= max_pages * page_size
  *   ws, ws_bytes   scratch of orthros_workspace_bytes(
- *                  ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after)
+ *                  ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after,
+ *                  head_map)
  * Other arguments as orthros_decode_pair.
  * Errors: EINVAL, EUNSUPPORTED (dtype or D), ECAPACITY, EWORKSPACE, EHIP.
  */
@@ -376,10 +383,17 @@ size_t orthros_layer_workspace_bytes(int B, int T, int T_out, int d_model,
  * Scratch bytes needed by orthros_global_xattn (op ORTHROS_OP_GLOBAL_XATTN,
  * max_len = T_in + T_out) or orthros_decode_pair (op ORTHROS_OP_DECODE_PAIR,
  * T_out = 1, max_len = max_len_after; also orthros_decode_pair_paged).
- * Returns 0 for an unknown op or invalid sizes. Pure host function.
+ * head_map [host] is the map the call will be given (NULL for the
+ * contiguous grouping): the query heads of each KV head are packed into
+ * groups, and the number and width of the groups size the scratch. The size
+ * depends on these arguments only, not on the device. Returns 0 for an
+ * unknown op, invalid sizes or an invalid map, and when the call needs no
+ * scratch for these sizes (ws may then be NULL). Pure host function; it
+ * leaves orthros_last_error() unchanged.
  */
 size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
-                               int T_out, int64_t max_len);
+                               int T_out, int64_t max_len,
+                               const int32_t *head_map);
 
 /* Static description of a status code. */
 const char *orthros_strerror(int code);

@@ -76,7 +76,8 @@ def lib():
     L.orthros_backward_workspace_bytes.restype = sz
     L.orthros_layer_workspace_bytes.argtypes = [i32] * 7
     L.orthros_layer_workspace_bytes.restype = sz
-    L.orthros_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i64]
+    L.orthros_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i64,
+                                          vp]
     L.orthros_workspace_bytes.restype = sz
     L.orthros_strerror.argtypes = [i32]
     L.orthros_strerror.restype = ctypes.c_char_p
@@ -121,15 +122,53 @@ def _dev(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _vecs(n, *named):
+    """fp32 vectors of n entries (alpha/beta: Hq*D) on the GPU, given as
+    (tensor, name) pairs; every size is checked before any device check."""
+    for t, name in named:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} elements (Hq*D), got "
+                             f"{t.numel()}")
+    return [_dev(t, name, torch.float32) for t, name in named]
+
+
+def _lens(t, B, name="cache_len"):
+    """Checks the int32 [B] cache lengths' size (before any device check)
+    and returns the tensor."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.int32 or t.numel() != B:
+        raise ValueError(f"{name} must be int32 with B={B} entries, got "
+                         f"{t.dtype} with {t.numel()}")
+    return t
+
+
 def _stream(stream, like):
     if stream is None:
         stream = torch.cuda.current_stream(like.device)
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _map(head_map):
+def _scratch(nbytes, device, stream):
+    """Scratch allocated here for one call. The caching allocator ties a
+    tensor to the stream current at allocation; when the call runs on
+    another stream, the block must not be handed out again until that
+    stream's work is done, hence record_stream."""
+    ws = workspace(nbytes, device)
+    if stream is not None:
+        ws.record_stream(stream)
+    return ws
+
+
+def _map(head_map, Hq=None):
+    """Host int32 copy of the head map (the library reads Hq entries)."""
     if head_map is None:
         return None, None
+    if Hq is not None and len(head_map) != Hq:
+        raise ValueError(f"head_map must have Hq={Hq} entries, got "
+                         f"{len(head_map)}")
     arr = (ctypes.c_int32 * len(head_map))(*[int(x) for x in head_map])
     return ctypes.cast(arr, ctypes.c_void_p), arr
 
@@ -146,9 +185,10 @@ def orthros_abi_version():
     return int(lib().orthros_abi_version())
 
 
-def orthros_workspace_bytes(op, B, Hq, Hkv, D, T_out, max_len):
+def orthros_workspace_bytes(op, B, Hq, Hkv, D, T_out, max_len, head_map=None):
+    hm, _keep = _map(head_map, Hq)
     return int(lib().orthros_workspace_bytes(op, B, Hq, Hkv, D, T_out,
-                                             int(max_len)))
+                                             int(max_len), hm))
 
 
 def workspace(nbytes, device):
@@ -164,9 +204,10 @@ def orthros_kv_append(k_cache, v_cache, cache_len, k_new, v_new, stream=None):
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache shapes differ")
     dt = k_cache.dtype
+    cl_p = _dev(_lens(cache_len, B), "cache_len", torch.int32)
     _check(lib().orthros_kv_append(
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
-        _dev(cache_len, "cache_len", torch.int32), _dev(k_new, "k_new", dt),
+        cl_p, _dev(k_new, "k_new", dt),
         _dev(v_new, "v_new", dt), B, n_new, Hkv, D, cap, _dtype_code(k_cache),
         _stream(stream, k_cache)))
 
@@ -180,10 +221,10 @@ def orthros_swa_prefill(q_pre, alpha, beta, k_cache, v_cache, o, W,
     if o.shape != q_pre.shape:
         raise ValueError("o must have q_pre's shape")
     dt = q_pre.dtype
-    hm, _keep = _map(head_map)
+    a_p, b_p = _vecs(Hq * D, (alpha, "alpha"), (beta, "beta"))
+    hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_swa_prefill(
-        _dev(q_pre, "q_pre", dt), _dev(alpha, "alpha", torch.float32),
-        _dev(beta, "beta", torch.float32), _dev(k_cache, "k_cache", dt),
+        _dev(q_pre, "q_pre", dt), a_p, b_p, _dev(k_cache, "k_cache", dt),
         _dev(v_cache, "v_cache", dt), _dev(o, "o", dt), B, T, Hq, Hkv, D, cap,
         int(W), hm, _dtype_code(q_pre), _stream(stream, q_pre)))
 
@@ -197,14 +238,14 @@ def orthros_global_xattn(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, T_in,
     if o_x.shape != qx_pre.shape:
         raise ValueError("o_x must have qx_pre's shape")
     dt = qx_pre.dtype
+    ax_p, bx_p = _vecs(Hq * D, (alpha_x, "alpha_x"), (beta_x, "beta_x"))
     if ws is None:
         need = orthros_workspace_bytes(ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D,
-                                       T_out, int(T_in) + T_out)
-        ws = workspace(need, qx_pre.device) if need else None
-    hm, _keep = _map(head_map)
+                                       T_out, int(T_in) + T_out, head_map)
+        ws = _scratch(need, qx_pre.device, stream) if need else None
+    hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_global_xattn(
-        _dev(qx_pre, "qx_pre", dt), _dev(alpha_x, "alpha_x", torch.float32),
-        _dev(beta_x, "beta_x", torch.float32), _dev(k_cache, "k_cache", dt),
+        _dev(qx_pre, "qx_pre", dt), ax_p, bx_p, _dev(k_cache, "k_cache", dt),
         _dev(v_cache, "v_cache", dt), _dev(o_x, "o_x", dt), B, int(T_in),
         T_out, Hq, Hkv, D, cap, hm, _dtype_code(qx_pre), _dev(ws, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(),
@@ -223,19 +264,20 @@ def orthros_decode_pair(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
     if qx_pre.shape != q_pre.shape or o.shape != q_pre.shape or o_x.shape != q_pre.shape:
         raise ValueError("q_pre, qx_pre, o, o_x must all be [B, Hq, D]")
     dt = q_pre.dtype
+    _lens(cache_len, B)
+    aff = _vecs(Hq * D, (alpha, "alpha"), (beta, "beta"),
+                (alpha_x, "alpha_x"), (beta_x, "beta_x"))
+    cl_p = _dev(cache_len, "cache_len", torch.int32)
     if ws is None:
         need = orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D,
-                                       1, int(max_len_after))
-        ws = workspace(need, q_pre.device) if need else None
-    hm, _keep = _map(head_map)
-    f32 = torch.float32
+                                       1, int(max_len_after), head_map)
+        ws = _scratch(need, q_pre.device, stream) if need else None
+    hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_decode_pair(
-        _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt),
-        _dev(alpha, "alpha", f32), _dev(beta, "beta", f32),
-        _dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32),
+        _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt), *aff,
         _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
-        _dev(cache_len, "cache_len", torch.int32), _dev(o, "o", dt),
+        cl_p, _dev(o, "o", dt),
         _dev(o_x, "o_x", dt), B, Hq, Hkv, D, cap, int(max_len_after), int(W),
         hm, _dtype_code(q_pre), _dev(ws, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(),
@@ -246,8 +288,10 @@ def _paged(k_pool, v_pool, block_table):
     n_pages, Hkv, page_size, D = k_pool.shape
     if v_pool.shape != k_pool.shape:
         raise ValueError("k_pool and v_pool shapes differ")
-    if block_table.dim() != 2:
-        raise ValueError("block_table must be [B, max_pages]")
+    if not isinstance(block_table, torch.Tensor) or block_table.dim() != 2:
+        raise ValueError("block_table must be a [B, max_pages] tensor")
+    if block_table.dtype != torch.int32:
+        raise ValueError(f"block_table must be int32, got {block_table.dtype}")
     return n_pages, Hkv, page_size, D, block_table.shape[1]
 
 
@@ -262,10 +306,11 @@ def orthros_kv_append_paged(k_pool, v_pool, block_table, cache_len, k_new,
     if block_table.shape[0] != B:
         raise ValueError("block_table must have B rows")
     dt = k_pool.dtype
+    cl_p = _dev(_lens(cache_len, B), "cache_len", torch.int32)
     _check(lib().orthros_kv_append_paged(
         _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt), n_pages,
         page_size, _dev(block_table, "block_table", torch.int32), max_pages,
-        _dev(cache_len, "cache_len", torch.int32), _dev(k_new, "k_new", dt),
+        cl_p, _dev(k_new, "k_new", dt),
         _dev(v_new, "v_new", dt), B, n_new, Hkv, D, _dtype_code(k_pool),
         _stream(stream, k_pool)))
 
@@ -286,20 +331,21 @@ def orthros_decode_pair_paged(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
     if block_table.shape[0] != B:
         raise ValueError("block_table must have B rows")
     dt = q_pre.dtype
+    _lens(cache_len, B)
+    aff = _vecs(Hq * D, (alpha, "alpha"), (beta, "beta"),
+                (alpha_x, "alpha_x"), (beta_x, "beta_x"))
+    cl_p = _dev(cache_len, "cache_len", torch.int32)
     if ws is None:
         need = orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D,
-                                       1, int(max_len_after))
-        ws = workspace(need, q_pre.device) if need else None
-    hm, _keep = _map(head_map)
-    f32 = torch.float32
+                                       1, int(max_len_after), head_map)
+        ws = _scratch(need, q_pre.device, stream) if need else None
+    hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_decode_pair_paged(
-        _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt),
-        _dev(alpha, "alpha", f32), _dev(beta, "beta", f32),
-        _dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32),
+        _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt), *aff,
         _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
         _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt), n_pages,
         page_size, _dev(block_table, "block_table", torch.int32), max_pages,
-        _dev(cache_len, "cache_len", torch.int32), _dev(o, "o", dt),
+        cl_p, _dev(o, "o", dt),
         _dev(o_x, "o_x", dt), B, Hq, Hkv, D, int(max_len_after), int(W), hm,
         _dtype_code(q_pre), _dev(ws, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(),
@@ -337,14 +383,16 @@ def orthros_attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
     g.setdefault("dv", torch.empty((B, T, Hkv, D), dtype=bf, device=dev))
     for name in ("d_alpha", "d_beta", "d_alpha_x", "d_beta_x"):
         g.setdefault(name, torch.empty(Hq * D, dtype=f32, device=dev))
+    aff = (_vecs(Hq * D, (alpha, "alpha"), (beta, "beta"),
+                 (alpha_x, "alpha_x"), (beta_x, "beta_x")) if T_out else
+           _vecs(Hq * D, (alpha, "alpha"), (beta, "beta")) +
+           [_dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32)])
     if ws is None:
-        ws = workspace(orthros_backward_workspace_bytes(B, T, T_out, Hq, Hkv, D),
-                       dev)
-    hm, _keep = _map(head_map)
+        ws = _scratch(orthros_backward_workspace_bytes(B, T, T_out, Hq, Hkv, D),
+                      dev, stream)
+    hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_attn_backward(
-        _dev(q_pre, "q_pre", bf), _dev(qx_pre, "qx_pre", bf),
-        _dev(alpha, "alpha", f32), _dev(beta, "beta", f32),
-        _dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32),
+        _dev(q_pre, "q_pre", bf), _dev(qx_pre, "qx_pre", bf), *aff,
         _dev(k_cache, "k_cache", bf), _dev(v_cache, "v_cache", bf),
         _dev(o, "o", bf), _dev(o_x, "o_x", bf), _dev(d_o, "d_o", bf),
         _dev(d_ox, "d_ox", bf), _dev(g["dq_pre"], "dq_pre", bf),
@@ -382,17 +430,21 @@ def orthros_layer_forward(x, w_q, w_k, w_v, w_o, alpha, beta, alpha_x,
                          "x2 and [d_model, Hq*D]")
     if y.shape != x.shape:
         raise ValueError("y must have x's shape")
-    if ws is None:
-        ws = workspace(orthros_layer_workspace_bytes(B, T, int(T_out), d_model,
-                                                     Hq, Hkv, D), x.device)
     bf = torch.bfloat16
     f32 = torch.float32
+    aff = (_vecs(Hq * D, (alpha, "alpha"), (beta, "beta"),
+                 (alpha_x, "alpha_x"), (beta_x, "beta_x")) if int(T_out) else
+           _vecs(Hq * D, (alpha, "alpha"), (beta, "beta")) +
+           [_dev(alpha_x, "alpha_x", f32), _dev(beta_x, "beta_x", f32)])
+    cl_p = _dev(_lens(cache_len, B), "cache_len", torch.int32)
+    if ws is None:
+        ws = _scratch(orthros_layer_workspace_bytes(B, T, int(T_out), d_model,
+                                                    Hq, Hkv, D), x.device,
+                      stream)
     _check(lib().orthros_layer_forward(
         _dev(x, "x", bf), _dev(w_q, "w_q", bf), _dev(w_k, "w_k", bf),
-        _dev(w_v, "w_v", bf), _dev(w_o, "w_o", bf), _dev(alpha, "alpha", f32),
-        _dev(beta, "beta", f32), _dev(alpha_x, "alpha_x", f32),
-        _dev(beta_x, "beta_x", f32), _dev(k_cache, "k_cache", bf),
-        _dev(v_cache, "v_cache", bf), _dev(cache_len, "cache_len", torch.int32),
+        _dev(w_v, "w_v", bf), _dev(w_o, "w_o", bf), *aff,
+        _dev(k_cache, "k_cache", bf), _dev(v_cache, "v_cache", bf), cl_p,
         _dev(y, "y", bf), B, T, int(T_out), d_model, Hq, Hkv, D, cap, int(W),
         _dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream, x)))
 

@@ -2,7 +2,8 @@
 
 Usage: python -m long_context_prefill_swa_amd.build   (or python build.py)
 Objects go to _build/ beside this file; the library to
-long_context_prefill_swa_amd/liborthros.so.
+long_context_prefill_swa_amd/liborthros.so. The benchmark's shader-clock
+probe is built beside it as libclock_probe.so (not part of the library).
 """
 import concurrent.futures as cf
 import os
@@ -14,9 +15,11 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liborthros.so")
+PROBE_LIB = os.path.join(HERE, "libclock_probe.so")
+PROBE_SRC = "clock_probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kv_append.hip", "rowwise.hip", "splitkv_mfma.hip",
+SOURCES = ["kv_append.hip", "rowwise.hip", "splitkv_mfma.hip", "splitkv_plan.cpp",
            "band_mfma.hip", "band_roll.hip", "band_persist.hip",
            "band_bwd.hip", "orthros_api.cpp", "gemm.cpp", "layer.cpp"]
 
@@ -42,17 +45,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out, libs, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs,
-           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
+           "-L/opt/rocm/lib", *libs, "-Wl,-rpath,/opt/rocm/lib"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [PROBE_SRC]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:-1], LIB, ["-lhipblaslt"], verbose)
+    _link(objs[-1:], PROBE_LIB, [], verbose)
     return LIB
 
 

@@ -48,7 +48,7 @@ bool layer_ws(int T, int T_out, int Hq, int Hkv, int D, LayerWs *w) {
   w->o_cat = off;
   off += align256(M * Hq * D * 2);
   w->xattn_bytes = T_out > 0 ? orthros_workspace_bytes(ORTHROS_OP_GLOBAL_XATTN, 1, Hq,
-                                                       Hkv, D, T_out, T)
+                                                       Hkv, D, T_out, T, nullptr)
                              : 0;
   w->xattn_ws = off;
   off += align256(w->xattn_bytes);

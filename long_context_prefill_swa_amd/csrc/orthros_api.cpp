@@ -195,17 +195,22 @@ const char *orthros_strerror(int code) {
 const char *orthros_last_error(void) { return g_msg; }
 
 size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
-                               int T_out, int64_t max_len) {
+                               int T_out, int64_t max_len,
+                               const int32_t *head_map) {
   if (B < 1 || T_out < 1 || max_len < 1 || D < 1 || D > ORTHROS_MAX_D)
     return 0;
-  if (Hq < 1 || Hkv < 1 || Hq > ORTHROS_MAX_HEADS || Hkv > ORTHROS_MAX_HEADS ||
-      Hq % Hkv != 0)
+  if (Hq < 1 || Hkv < 1 || Hq > ORTHROS_MAX_HEADS || Hkv > ORTHROS_MAX_HEADS)
     return 0;
+  // The same head grouping the calls build from (head_map, Hq, Hkv): the
+  // number of groups and the group width size the partials.
+  // A pure query: the caller's last error message is left as it was.
   HeadMap map;
   HeadGroups g;
-  const int saved = g_msg[0];
-  if (build_maps(nullptr, Hq, Hkv, &map, &g) != ORTHROS_OK) return 0;
-  if (!saved) clear_error();
+  char saved[sizeof(g_msg)];
+  memcpy(saved, g_msg, sizeof(g_msg));
+  const int rc = build_maps(head_map, Hq, Hkv, &map, &g);
+  memcpy(g_msg, saved, sizeof(g_msg));
+  if (rc != ORTHROS_OK) return 0;
   SplitPlan p;
   if (op == ORTHROS_OP_GLOBAL_XATTN)
     p = plan_split(B, 1, T_out, g, D, max_len);

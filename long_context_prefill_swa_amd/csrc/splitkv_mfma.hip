@@ -34,8 +34,6 @@
 // (max, sum, unnormalised output) partial per row; a second kernel combines
 // the partials of all chunks with log-sum-exp weights, normalises, writes the
 // output rows and (decode) advances the cache length.
-#include <cstdlib>
-
 #include "common.h"
 
 namespace orthros {
@@ -520,40 +518,6 @@ __global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
 }
 
 }  // namespace
-
-int splitkv_rows(int n_streams, int n_pos, int gsize) {
-  return n_streams * n_pos * gsize;
-}
-
-// Keys per workgroup: a power of two from 256 to 2048, the largest that still
-// gives every compute unit its two resident workgroups (gfx950 parts have 256
-// compute units). At most 2048, so a chunk of a paged cache spans at most 64
-// pages (one block-table entry per lane). Long caches then run in whole rounds of long-lived
-// workgroups; short ones still spread over the whole chip. Depends on the
-// sizes only, so the workspace query needs no device.
-int splitkv_pick_chunk(int B, int n_groups, int64_t max_len) {
-  constexpr int64_t kResidentSlots = 2 * 256;
-  static const int max_chunk = [] {
-    const char *e = getenv("ORTHROS_SPLIT_CHUNK");
-    const int v = e ? atoi(e) : 0;
-    return (v == 256 || v == 512 || v == 1024 || v == 2048) ? v : 2048;
-  }();
-  int chunk = max_chunk;
-  while (chunk > 256 &&
-         (int64_t)B * n_groups * ((max_len + chunk - 1) / chunk) < kResidentSlots)
-    chunk /= 2;
-  return chunk;
-}
-
-// Workspace layout: per-batch old lengths (int32, padded to 256 bytes), then
-// (max, sum) float pairs of every partial, padded to 64 floats, then the
-// unnormalised output rows. Must agree with the offsets set by the caller.
-size_t splitkv_ws_bytes(int B, int n_groups, int rows, int n_chunks, int Dh) {
-  const size_t parts = (size_t)B * n_groups * n_chunks * rows;
-  const size_t len_bytes = ((size_t)B * 4 + 255) / 256 * 256;
-  const size_t ml_floats = (parts * 2 + 63) / 64 * 64;
-  return len_bytes + (ml_floats + parts * (size_t)Dh) * 4;
-}
 
 hipError_t launch_splitkv(const SplitKVArgs &a_in, const HeadGroups &groups,
                           hipStream_t stream) {

@@ -271,7 +271,7 @@ def layer(x, w_q, w_k, w_v, w_o, alpha, beta, alpha_x, beta_x, T_out, W,
 
 
 def attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k, v, d_o,
-                  d_ox, W, head_map=None):
+                  d_ox, W, head_map=None, heads=None, with_kv=True):
     """Gradients of both streams' outputs, fp64, row by row.
 
     Inputs as for ``swa`` and ``xattn`` (k, v [B, T, Hkv, D]; qx_pre
@@ -285,6 +285,11 @@ def attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k, v, d_o,
     dq_pre = alpha (.) dq, d_alpha = sum of dq (.) q_pre, d_beta = sum of dq.
     Returns a dict of dq_pre, dqx_pre, dk, dv, d_alpha, d_beta, d_alpha_x,
     d_beta_x (alpha/beta gradients [Hq*D]).
+
+    heads: optional list of query heads to evaluate (the entries of the
+    other heads stay zero); with_kv=False skips the dK, dV sums (left zero).
+    Each head's rows are independent of the others', so a subset gives that
+    subset's exact entries.
     """
     q_pre, qx_pre = _f64(q_pre), _f64(qx_pre)
     k, v, d_o, d_ox = _f64(k), _f64(v), _f64(d_o), _f64(d_ox)
@@ -310,8 +315,9 @@ def attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k, v, d_o,
         dp = V @ dO
         ds = p * (dp - p @ dp)
         dq = K.T @ ds * scale
-        g["dk"][b, lo:hi + 1, gkv] += np.outer(ds, q) * scale
-        g["dv"][b, lo:hi + 1, gkv] += np.outer(p, dO)
+        if with_kv:
+            g["dk"][b, lo:hi + 1, gkv] += np.outer(ds, q) * scale
+            g["dv"][b, lo:hi + 1, gkv] += np.outer(p, dO)
         return dq
 
     a2 = _f64(alpha).reshape(Hq, D)
@@ -319,7 +325,7 @@ def attn_backward(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k, v, d_o,
     ax2 = _f64(alpha_x).reshape(Hq, D)
     bx2 = _f64(beta_x).reshape(Hq, D)
     for b in range(B):
-        for h in range(Hq):
+        for h in (range(Hq) if heads is None else heads):
             for t in range(T):
                 dq = row(b, h, q_pre[b, t, h], a2[h], b2[h],
                          max(0, t - W + 1), t, d_o[b, t, h])

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.orthros_abi_version() == 5
+    assert L.orthros_abi_version() == 6
     for code in (OK, EINVAL, EUNSUP, ECAP, EWS, EHIP):
         assert L.orthros_strerror(code)
     assert b"unknown" in L.orthros_strerror(42)
@@ -130,7 +130,7 @@ def test_global_xattn_rejects(L):
     # split-KV path needs a workspace
     assert L.orthros_global_xattn(*args, None, 0, None) == EWS
     assert "workspace" in last(L)
-    need = L.orthros_workspace_bytes(1, 1, 4, 2, 128, 1, 101)
+    need = L.orthros_workspace_bytes(1, 1, 4, 2, 128, 1, 101, None)
     assert need > 0
     assert L.orthros_global_xattn(*args, FAKE, need - 1, None) == EWS
     bad = [FAKE] * 6 + [1, 100, 1, 4, 2, 128, 100, None, BF16]   # cap < T
@@ -158,7 +158,8 @@ def test_decode_pair_rejects(L):
 
 
 def test_workspace_bytes(L):
-    ws = L.orthros_workspace_bytes
+    def ws(*a):
+        return L.orthros_workspace_bytes(*a, None)
     assert ws(9, 1, 4, 2, 128, 1, 100) == 0            # unknown op
     assert ws(2, 0, 4, 2, 128, 1, 100) == 0            # empty batch
     d1 = ws(2, 64, 32, 8, 128, 1, 33024)
@@ -168,6 +169,54 @@ def test_workspace_bytes(L):
     assert ws(1, 4, 32, 8, 128, 2048, 8192) == 0
     # non-128 head dimensions run the generic kernel without workspace
     assert ws(1, 1, 2, 2, 16, 1, 64) == 0
+    # no map and Hq not a multiple of Hkv: invalid
+    assert ws(1, 1, 5, 2, 128, 1, 100) == 0
+
+
+def imap(m):
+    return (ctypes.c_int32 * len(m))(*m)
+
+
+@pytest.mark.parametrize("Hq,Hkv,hm", [
+    (6, 3, [0, 0, 0, 1, 2, 2]),       # uneven: 3, 1, 2 heads per KV head
+    (5, 2, [0, 1, 1, 0, 1]),          # Hq not a multiple of Hkv
+    (8, 2, [1, 1, 1, 1, 1, 1, 1, 0]),  # 7 heads on one KV head
+])
+def test_workspace_bytes_follows_the_head_map(L, Hq, Hkv, hm):
+    """The size the query returns for a map is the size the calls with that
+    map check against: one byte less is rejected with EWORKSPACE, the size
+    itself passes the workspace check (the call then fails only at the
+    launch, with no GPU here)."""
+    m = imap(hm)
+    for op in (1, 2):
+        need = L.orthros_workspace_bytes(op, 2, Hq, Hkv, 128, 1, 300, m)
+        assert need > 0
+        if op == 1:
+            def call(nb):
+                return L.orthros_global_xattn(
+                    *[FAKE] * 6, 2, 299, 1, Hq, Hkv, 128, 300, m, BF16,
+                    FAKE, nb, None)
+        else:
+            def call(nb):
+                return L.orthros_decode_pair(
+                    *[FAKE] * 10, FAKE, FAKE, FAKE, 2, Hq, Hkv, 128, 400, 300,
+                    16, m, BF16, FAKE, nb, None)
+        assert call(need - 1) == EWS, last(L)
+        assert call(need) in (OK, EHIP), last(L)
+    # the default grouping's size can be smaller than the map's
+    if Hq % Hkv == 0:
+        assert L.orthros_workspace_bytes(2, 2, Hq, Hkv, 128, 1, 300, None) <= \
+            L.orthros_workspace_bytes(2, 2, Hq, Hkv, 128, 1, 300, m)
+    bad = imap([0] * (Hq - 1) + [Hkv])    # entry out of range
+    assert L.orthros_workspace_bytes(2, 2, Hq, Hkv, 128, 1, 300, bad) == 0
+
+
+def test_workspace_query_keeps_the_last_error(L):
+    assert decode(L, W=0) == EINVAL
+    msg = last(L)
+    assert msg
+    L.orthros_workspace_bytes(2, 2, 4, 2, 128, 1, 100, imap([0, 0, 0, 5]))
+    assert last(L) == msg
 
 
 def paged_append(L, **kw):
@@ -232,7 +281,7 @@ def test_decode_pair_paged_rejects(L, kw, code, needle):
 
 
 def test_decode_pair_paged_workspace_matches_contiguous(L):
-    need = L.orthros_workspace_bytes(2, 2, 4, 2, 128, 1, 200)
+    need = L.orthros_workspace_bytes(2, 2, 4, 2, 128, 1, 200, None)
     assert need > 0
     assert paged_decode(L, ws=FAKE, ws_bytes=need - 16) == EWS
     assert paged_decode(L, B=0) == OK
@@ -309,3 +358,58 @@ def test_attn_backward_kv_head_without_queries_rejected(L):
     p, keep = hmap([0, 0, 0, 0])       # KV head 1 has no query head
     assert bwd(L, hmap=p) == EUNSUP and "none" in last(L)
     assert bwd(L, B=0) == OK
+
+
+# ---- binding-level size checks (CPU tensors: the size checks come before
+# ---- the device checks, so they run without a GPU) -------------------------
+
+def test_binding_checks_affine_and_length_sizes():
+    import torch
+
+    import long_context_prefill_swa_amd as lo
+    B, T, Hq, Hkv, D = 1, 8, 4, 2, 128
+    q = torch.zeros((B, T, Hq, D), dtype=torch.bfloat16)
+    kc = torch.zeros((B, Hkv, T, D), dtype=torch.bfloat16)
+    good = torch.zeros(Hq * D)
+    short = torch.zeros(Hq * D - 1)
+    with pytest.raises(ValueError, match="alpha must hold 512"):
+        lo.orthros_swa_prefill(q, short, good, kc, kc, q, 4)
+    with pytest.raises(ValueError, match="beta must hold 512"):
+        lo.orthros_swa_prefill(q, good, short, kc, kc, q, 4)
+    qx = torch.zeros((B, 1, Hq, D), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="alpha_x must hold 512"):
+        lo.orthros_global_xattn(qx, short, good, kc, kc, qx, T - 1)
+    qd = torch.zeros((B, Hq, D), dtype=torch.bfloat16)
+    kn = torch.zeros((B, Hkv, D), dtype=torch.bfloat16)
+    cl_bad = torch.zeros(B + 1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="cache_len must be int32 with B=1"):
+        lo.orthros_decode_pair(qd, qd, good, good, good, good, kn, kn, kc, kc,
+                               cl_bad, qd, qd, T, 4)
+    with pytest.raises(ValueError, match="beta_x must hold 512"):
+        lo.orthros_decode_pair(qd, qd, good, good, good, short, kn, kn, kc,
+                               kc, torch.zeros(B, dtype=torch.int32), qd, qd,
+                               T, 4)
+    with pytest.raises(ValueError, match="cache_len must be int32"):
+        lo.orthros_kv_append(kc, kc, torch.zeros(B, dtype=torch.int64),
+                             torch.zeros((B, 2, Hkv, D), dtype=torch.bfloat16),
+                             torch.zeros((B, 2, Hkv, D), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="head_map must have Hq=4"):
+        lo.orthros_workspace_bytes(lo.ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1,
+                                   T, head_map=[0, 1])
+
+
+def test_binding_checks_block_table():
+    import torch
+
+    import long_context_prefill_swa_amd as lo
+    pool = torch.zeros((4, 2, 32, 128), dtype=torch.bfloat16)
+    kn = torch.zeros((1, 1, 2, 128), dtype=torch.bfloat16)
+    cl = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="block_table must be int32"):
+        lo.orthros_kv_append_paged(pool, pool,
+                                   torch.zeros((1, 2), dtype=torch.int64), cl,
+                                   kn, kn)
+    with pytest.raises(ValueError, match="block_table must be a"):
+        lo.orthros_kv_append_paged(pool, pool,
+                                   torch.zeros(2, dtype=torch.int32), cl,
+                                   kn, kn)

@@ -87,25 +87,36 @@ def test_backward_custom_head_map():
     check(*case(1, 150, 6, 6, 3, 33, 610, head_map=hm))
 
 
-def test_backward_deterministic():
-    a1, _, _ = case(1, 333, 7, 8, 2, 50, 620)
-    a2, _, _ = case(1, 333, 7, 8, 2, 50, 620)
+def test_backward_xcd_block_order():
+    """(batch, KV head) pairs a multiple of 8, so every pair's workgroups
+    run on one XCD (the block renumbering the kernels use then): B = 2,
+    4 KV heads, every gradient compared in full."""
+    say("[backward] B=2 Hq=16 Hkv=4 (8 pairs)")
+    check(*case(2, 300, 20, 16, 4, 64, 630))
+
+
+def _bitwise(t):
+    return t.view(torch.int16) if t.dtype == BF else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("shape", [(1, 333, 7, 8, 2, 50, 620),
+                                   (2, 300, 20, 16, 4, 64, 640)])
+def test_backward_deterministic(shape):
+    a1, _, _ = case(*shape)
+    a2, _, _ = case(*shape)
     for name in a1:
         if a1[name] is not None:
-            x, y = a1[name], a2[name]
-            assert torch.equal(x.view(torch.int16) if x.dtype == BF else x.view(torch.int32),
-                               y.view(torch.int16) if y.dtype == BF else y.view(torch.int32)), name
+            assert torch.equal(_bitwise(a1[name]), _bitwise(a2[name])), name
 
 
-def test_backward_sft_shape_sampled():
+@pytest.fixture(scope="module")
+def sft_backward():
     """The SFT dual-stream shape the benchmark times (B=4, T=8192,
-    T_out=2048, W=1024, 32/8 heads): dq_pre on sampled base rows and dqx_pre
-    on sampled output rows (all heads), dK and dV on sampled keys of KV
-    head 0, for the first and last batch entries. (The scale-offset
-    gradients sum over every row; they are checked at the smaller shapes.)"""
+    T_out=2048, W=1024, 32/8 heads): forward outputs from the library,
+    seeded upstream gradients, one backward call."""
     from workloads import prefill_inputs, workload
     c, cid = workload("sft_dual_8k")
-    say(f"[backward full size] {c.name}")
+    say(f"[backward full size] {c.name}: GPU run")
     x = prefill_inputs(c, cid, DEV)
     kc, vc, _ = make_cache(x.k, x.v, c.T)
     o = torch.empty_like(x.q_pre)
@@ -118,21 +129,52 @@ def test_backward_sft_shape_sampled():
                                  x.alpha_x, x.beta_x, kc, vc, o, ox, d_o,
                                  d_ox, c.W)
     torch.cuda.synchronize()
+    args = [f64(t) for t in (x.q_pre, x.qx_pre, x.alpha, x.beta, x.alpha_x,
+                             x.beta_x, x.k, x.v, d_o, d_ox)]
+    host = {k: (f64(v) if v is not None else None) for k, v in g.items()}
+    return c, args, host
+
+
+def test_backward_sft_shape_sampled(sft_backward):
+    """dq_pre on sampled base rows and dqx_pre on sampled output rows (all
+    heads), dK and dV on sampled keys of three KV heads, for the first and
+    last batch entries."""
+    c, args, g = sft_backward
     rng = np.random.default_rng(77)
     rows = sorted({0, 1, c.W - 1, c.W, c.T_in - 1, c.T_in, c.T - 1,
                    *map(int, rng.integers(0, c.T, 6))})
     out_rows = sorted({0, 1, c.T_out - 1, *map(int, rng.integers(0, c.T_out, 3))})
     keys = [0, 1000, c.T_in, c.T - 1]
-    args = [f64(t) for t in (x.q_pre, x.qx_pre, x.alpha, x.beta, x.alpha_x,
-                             x.beta_x, x.k, x.v, d_o, d_ox)]
     for b in (0, c.B - 1):
-        dq, dqx, dk, dv = oracle.attn_backward_sampled(*args, c.W, b, rows,
-                                                       out_rows, keys, 0)
-        for name, got, ref in (
-                ("dq_pre", g["dq_pre"][b, rows], dq),
-                ("dqx_pre", g["dqx_pre"][b, out_rows], dqx),
-                ("dk", g["dk"][b, keys, 0], dk),
-                ("dv", g["dv"][b, keys, 0], dv)):
-            scale = max(1.0, float(np.abs(ref).max()))
-            compare(got, ref, BF, f"b={b} {name} (largest {scale:.2f})",
-                    tol=(TOL[BF][0] * scale, TOL[BF][1]))
+        for kvh in (0, 3, 7):
+            dq, dqx, dk, dv = oracle.attn_backward_sampled(
+                *args, c.W, b, rows if kvh == 0 else [],
+                out_rows if kvh == 0 else [], keys, kvh)
+            checks = [("dk", g["dk"][b, keys, kvh], dk),
+                      ("dv", g["dv"][b, keys, kvh], dv)]
+            if kvh == 0:
+                checks += [("dq_pre", g["dq_pre"][b, rows], dq),
+                           ("dqx_pre", g["dqx_pre"][b, out_rows], dqx)]
+            for name, got, ref in checks:
+                scale = max(1.0, float(np.abs(ref).max()))
+                compare(got, ref, BF,
+                        f"b={b} kv head {kvh} {name} (largest {scale:.2f})",
+                        tol=(TOL[BF][0] * scale, TOL[BF][1]))
+
+
+@pytest.mark.parametrize("heads", [(0, 13), (22, 31)])
+def test_backward_sft_shape_scale_offset_gradients(sft_backward, heads):
+    """d_alpha, d_beta, d_alpha_x and d_beta_x of two query heads at the
+    SFT shape: each is a sum over all 4 x 8192 base rows (or 4 x 2048
+    output rows) of that head, so the oracle evaluates every row of those
+    heads (their entries are independent of the other heads)."""
+    c, args, g = sft_backward
+    Hq, D = c.Hq, c.D
+    say(f"[backward full size] scale-offset gradients of heads {heads}")
+    ref = oracle.attn_backward(*args, c.W, heads=list(heads), with_kv=False)
+    for name in ("d_alpha", "d_beta", "d_alpha_x", "d_beta_x"):
+        got = g[name].reshape(Hq, D)[list(heads)]
+        want = ref[name].reshape(Hq, D)[list(heads)]
+        scale = max(1.0, float(np.abs(want).max()))
+        compare(got, want, BF, f"{name} heads {heads} (largest {scale:.2f})",
+                tol=(TOL[BF][0] * scale, TOL[BF][1]))

@@ -600,3 +600,24 @@ def test_backward_sampled_equals_full():
             np.testing.assert_allclose(dqx, full["dqx_pre"][b, out_rows], atol=1e-12)
             np.testing.assert_allclose(dk, full["dk"][b, keys, g], atol=1e-12)
             np.testing.assert_allclose(dv, full["dv"][b, keys, g], atol=1e-12)
+
+
+def test_backward_head_subset_equals_autograd():
+    """A subset of query heads (and no dK/dV sums) gives those heads' exact
+    entries of every per-head gradient, compared with torch autograd; the
+    other heads' entries and dK/dV stay zero."""
+    B, T, T_out, Hq, Hkv, D, W = 2, 19, 4, 4, 2, 8, 5
+    args = grad_case(B, T, T_out, Hq, Hkv, D, 931)
+    heads = [1, 3]
+    got = oracle.attn_backward(*args, W, heads=heads, with_kv=False)
+    ref = torch_streams_grad(*args, W)
+    for name in ("d_alpha", "d_beta", "d_alpha_x", "d_beta_x"):
+        g2, r2 = got[name].reshape(Hq, D), ref[name].reshape(Hq, D)
+        np.testing.assert_allclose(g2[heads], r2[heads], rtol=1e-10,
+                                   atol=1e-11, err_msg=name)
+        assert (g2[[0, 2]] == 0).all()
+    for name in ("dq_pre", "dqx_pre"):
+        np.testing.assert_allclose(got[name][:, :, heads], ref[name][:, :, heads],
+                                   rtol=1e-10, atol=1e-11, err_msg=name)
+        assert (got[name][:, :, [0, 2]] == 0).all()
+    assert (got["dk"] == 0).all() and (got["dv"] == 0).all()
