@@ -216,6 +216,37 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
                         int dtype, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * orthros_decode_pair_noalloc - orthros_decode_pair without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory around the call: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc. The split-KV partials go to
+ * a static device array of ORTHROS_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every device it runs on until the process ends (its address is
+ * looked up on the first call on a device). The call allocates nothing and
+ * calls no allocating routine.
+ *
+ * Sizes whose scratch (orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, ...,
+ * head_map)) exceeds ORTHROS_NOALLOC_SCRATCH_BYTES are rejected with
+ * ORTHROS_EWORKSPACE before anything is launched; 64 MiB covers, e.g.,
+ * B = 64 sequences of 32/8 heads up to about 60K cached keys. Every call on
+ * a device shares that device's array: calls that overlap in time on one
+ * device (different streams, no ordering) race and give wrong results. The
+ * array needs no initial contents (every byte a call reads it wrote first).
+ * Arguments, results and errors otherwise as orthros_decode_pair.
+ */
+#define ORTHROS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int orthros_decode_pair_noalloc(const void *q_pre, const void *qx_pre,
+                                const float *alpha, const float *beta,
+                                const float *alpha_x, const float *beta_x,
+                                const void *k_new, const void *v_new,
+                                void *k_cache, void *v_cache,
+                                int32_t *cache_len, void *o, void *o_x, int B,
+                                int Hq, int Hkv, int D, int64_t cap,
+                                int64_t max_len_after, int W,
+                                const int32_t *head_map, int dtype,
+                                void *stream);
+
+/*
  * Paged K/V cache (variable-length batched decoding).
  *
  * Pages: paper text §3.3 (decoding is bound by memory I/O; batched decoding

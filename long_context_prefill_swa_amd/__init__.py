@@ -20,7 +20,8 @@ __all__ = [
     "ORTHROS_F32", "ORTHROS_BF16", "ORTHROS_OP_GLOBAL_XATTN",
     "ORTHROS_OP_DECODE_PAIR", "OrthrosError", "lib", "library_path",
     "orthros_kv_append", "orthros_swa_prefill", "orthros_global_xattn",
-    "orthros_decode_pair", "orthros_kv_append_paged",
+    "orthros_decode_pair", "orthros_decode_pair_noalloc",
+    "orthros_kv_append_paged", "ORTHROS_NOALLOC_SCRATCH_BYTES",
     "orthros_decode_pair_paged", "orthros_workspace_bytes",
     "orthros_check_device_errors", "orthros_abi_version",
     "orthros_strerror", "orthros_last_error", "workspace",
@@ -30,6 +31,7 @@ ORTHROS_F32 = 0
 ORTHROS_BF16 = 1
 ORTHROS_OP_GLOBAL_XATTN = 1
 ORTHROS_OP_DECODE_PAIR = 2
+ORTHROS_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "liborthros.so")
@@ -62,6 +64,8 @@ def lib():
     L.orthros_decode_pair.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       vp, vp, vp, i32, i32, i32, i32, i64,
                                       i64, i32, vp, i32, vp, sz, vp]
+    L.orthros_decode_pair_noalloc.argtypes = [vp] * 13 + [i32] * 4 + [
+        i64, i64, i32, vp, i32, vp]
     L.orthros_kv_append_paged.argtypes = [vp, vp, i64, i32, vp, i32, vp, vp,
                                           vp, i32, i32, i32, i32, i32, vp]
     L.orthros_decode_pair_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
@@ -87,6 +91,7 @@ def lib():
     L.orthros_abi_version.argtypes = []
     for name in ("orthros_kv_append", "orthros_swa_prefill",
                  "orthros_global_xattn", "orthros_decode_pair",
+                 "orthros_decode_pair_noalloc",
                  "orthros_kv_append_paged", "orthros_decode_pair_paged",
                  "orthros_check_device_errors", "orthros_abi_version"):
         getattr(L, name).restype = i32
@@ -281,6 +286,36 @@ def orthros_decode_pair(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
         _dev(o_x, "o_x", dt), B, Hq, Hkv, D, cap, int(max_len_after), int(W),
         hm, _dtype_code(q_pre), _dev(ws, "ws"),
         0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream, q_pre)))
+
+
+def orthros_decode_pair_noalloc(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
+                                k_new, v_new, k_cache, v_cache, cache_len, o,
+                                o_x, max_len_after, W, head_map=None,
+                                stream=None):
+    """orthros_decode_pair with no workspace and no allocation: the library's
+    static per-device scratch (ORTHROS_NOALLOC_SCRATCH_BYTES) holds the
+    partials. Calls overlapping in time on one device race."""
+    B, Hq, D = q_pre.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    if tuple(k_cache.shape) != (B, Hkv, cap, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [B, Hkv, cap, D]")
+    if tuple(k_new.shape) != (B, Hkv, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, Hkv, D]")
+    if qx_pre.shape != q_pre.shape or o.shape != q_pre.shape or o_x.shape != q_pre.shape:
+        raise ValueError("q_pre, qx_pre, o, o_x must all be [B, Hq, D]")
+    dt = q_pre.dtype
+    _lens(cache_len, B)
+    aff = _vecs(Hq * D, (alpha, "alpha"), (beta, "beta"),
+                (alpha_x, "alpha_x"), (beta_x, "beta_x"))
+    cl_p = _dev(cache_len, "cache_len", torch.int32)
+    hm, _keep = _map(head_map, Hq)
+    _check(lib().orthros_decode_pair_noalloc(
+        _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt), *aff,
+        _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        cl_p, _dev(o, "o", dt), _dev(o_x, "o_x", dt), B, Hq, Hkv, D, cap,
+        int(max_len_after), int(W), hm, _dtype_code(q_pre),
         _stream(stream, q_pre)))
 
 

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/orthros.h"
 #include "common.h"
@@ -371,14 +372,52 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
   return ORTHROS_OK;
 }
 
-int orthros_decode_pair(const void *q_pre, const void *qx_pre,
-                        const float *alpha, const float *beta,
-                        const float *alpha_x, const float *beta_x,
-                        const void *k_new, const void *v_new, void *k_cache,
-                        void *v_cache, int32_t *cache_len, void *o, void *o_x,
-                        int B, int Hq, int Hkv, int D, int64_t cap,
-                        int64_t max_len_after, int W, const int32_t *head_map,
-                        int dtype, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- scratch of the no-allocation decode pair -------------------------------
+// A static device array, one copy per device the library runs on, alive until
+// the process ends. Host code never uses the array's name as an address (in
+// host code it is a stand-in, not a device pointer): the device address is
+// looked up once per device with hipGetSymbolAddress and kept.
+constexpr size_t kScratchBytes = ORTHROS_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current).
+hipError_t scratch_ptr(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// The decode pair step. With from_scratch, the split-KV partials go to the
+// static scratch array instead of the caller's ws (which is then ignored).
+int decode_pair_impl(const void *q_pre, const void *qx_pre,
+                     const float *alpha, const float *beta,
+                     const float *alpha_x, const float *beta_x,
+                     const void *k_new, const void *v_new, void *k_cache,
+                     void *v_cache, int32_t *cache_len, void *o, void *o_x,
+                     int B, int Hq, int Hkv, int D, int64_t cap,
+                     int64_t max_len_after, int W, const int32_t *head_map,
+                     int dtype, void *ws, size_t ws_bytes, bool from_scratch,
+                     void *stream) {
   clear_error();
   int rc = check_dtype_d(dtype, D);
   if (rc) return rc;
@@ -407,11 +446,22 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
       dtype, D, max_len_after, {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new, v_new,
                  k_cache, v_cache, o, o_x});
   const SplitPlan plan = plan_split(B, 2, 1, groups, D, max_len_after);
+  hipError_t e;
+  if (mfma && plan.use && from_scratch) {
+    if (plan.ws_bytes > kScratchBytes)
+      return fail(ORTHROS_EWORKSPACE,
+                  "these sizes need %zu bytes of scratch; the no-allocation "
+                  "decode pair holds %zu (use orthros_decode_pair with a "
+                  "workspace)", plan.ws_bytes, kScratchBytes);
+    e = scratch_ptr(&ws);
+    if (e != hipSuccess) return hip_fail("scratch symbol", e);
+    ws_bytes = kScratchBytes;
+  }
   if (mfma && plan.use && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)))
     return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
                 plan.ws_bytes, ws ? ws_bytes : (size_t)0);
   int *flag = nullptr;
-  hipError_t e = device_flag_ptr(&flag);
+  e = device_flag_ptr(&flag);
   if (e != hipSuccess) return hip_fail("device flag", e);
   if (mfma && plan.use) {
     SplitKVArgs a = {};
@@ -459,6 +509,40 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
   if (e == hipSuccess) e = launch_len_bump(cache_len, B, 1, max_len_after, st);
   if (e != hipSuccess) return hip_fail("decode_pair launch", e);
   return ORTHROS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int orthros_decode_pair(const void *q_pre, const void *qx_pre,
+                        const float *alpha, const float *beta,
+                        const float *alpha_x, const float *beta_x,
+                        const void *k_new, const void *v_new, void *k_cache,
+                        void *v_cache, int32_t *cache_len, void *o, void *o_x,
+                        int B, int Hq, int Hkv, int D, int64_t cap,
+                        int64_t max_len_after, int W, const int32_t *head_map,
+                        int dtype, void *ws, size_t ws_bytes, void *stream) {
+  return decode_pair_impl(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
+                          v_new, k_cache, v_cache, cache_len, o, o_x, B, Hq,
+                          Hkv, D, cap, max_len_after, W, head_map, dtype, ws,
+                          ws_bytes, false, stream);
+}
+
+int orthros_decode_pair_noalloc(const void *q_pre, const void *qx_pre,
+                                const float *alpha, const float *beta,
+                                const float *alpha_x, const float *beta_x,
+                                const void *k_new, const void *v_new,
+                                void *k_cache, void *v_cache,
+                                int32_t *cache_len, void *o, void *o_x, int B,
+                                int Hq, int Hkv, int D, int64_t cap,
+                                int64_t max_len_after, int W,
+                                const int32_t *head_map, int dtype,
+                                void *stream) {
+  return decode_pair_impl(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
+                          v_new, k_cache, v_cache, cache_len, o, o_x, B, Hq,
+                          Hkv, D, cap, max_len_after, W, head_map, dtype,
+                          nullptr, 0, true, stream);
 }
 
 // Shared checks of the paged-cache arguments; on success *log2 = log2 of

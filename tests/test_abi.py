@@ -413,3 +413,19 @@ def test_binding_checks_block_table():
         lo.orthros_kv_append_paged(pool, pool,
                                    torch.zeros(2, dtype=torch.int32), cl,
                                    kn, kn)
+
+
+def test_noalloc_decode_pair_rejects_sizes_beyond_its_scratch(L):
+    """Sizes whose split-KV scratch exceeds the static array are rejected on
+    the host (EWORKSPACE), before anything is launched."""
+    limit = 64 << 20
+    assert L.orthros_workspace_bytes(2, 64, 32, 8, 128, 1, 200000, None) > limit
+    rc = L.orthros_decode_pair_noalloc(*[FAKE] * 10, FAKE, FAKE, FAKE, 64, 32,
+                                       8, 128, 200001, 200000, 2048, None,
+                                       BF16, None)
+    assert rc == EWS
+    assert "no-allocation" in last(L)
+    # ordinary argument errors come first, as in orthros_decode_pair
+    assert L.orthros_decode_pair_noalloc(*[FAKE] * 10, FAKE, FAKE, FAKE, 2, 4,
+                                         2, 128, 100, 101, 16, None, BF16,
+                                         None) == ECAP
