@@ -372,12 +372,12 @@ def main():
             "algorithmic_bytes_256_steps": kv_read + small,
             "notes": "each 256-step pass follows a 1 GiB write that evicts "
                      "the MALL"}
-        # The decode pair's dominant kernel is the split-KV stream; its
-        # launch is bracketed together with the short merge kernel.
+        # The decode pair is one split-KV launch per step (the merge and
+        # the length bump run in the same launch).
         sha_s = kernel_sha(SPLIT_SRC)
         step_bytes = (kv_read + small) / n_dec
         out["roofline_decode"] = {
-            "kernel": "splitkv_kernel + splitkv_merge_kernel (decode pair step, B=64)",
+            "kernel": "splitkv_kernel (decode pair step, B=64)",
             "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM_GBPS,
             "unit": "GB/s", "frac": gbps / PEAK_HBM_GBPS,
             "traffic": traffic_from_profile("splitkv_decode_b64", sha_s),

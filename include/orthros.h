@@ -50,6 +50,15 @@
  *    stream is. Calls that share buffers must be ordered by the caller.
  *  * Zero-sized work (B == 0, T == 0, n_new == 0) returns ORTHROS_OK and
  *    launches nothing.
+ *  * Split-KV workspaces (the ws of orthros_global_xattn and the decode
+ *    pairs) begin with arrival counters: the first
+ *    orthros_workspace_counter_bytes(...) bytes must be zero when a call
+ *    starts, and every call leaves them zero. Zero a workspace once after
+ *    allocating it (hipMemset); it can then serve any number of calls with
+ *    the same B and head grouping. Zero it again before a call with more
+ *    (batch entry, head group) pairs, whose counters would overlap bytes an
+ *    earlier call used for partial results. The rest of the workspace is
+ *    scratch: its contents on entry are ignored and left undefined.
  *  * Device-side capacity faults (a cache length that would exceed cap)
  *    never write out of bounds: the affected batch entry is skipped and a
  *    sticky device flag is raised, reported by orthros_check_device_errors.
@@ -64,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ORTHROS_ABI_VERSION 6
+#define ORTHROS_ABI_VERSION 7
 
 /* dtype codes */
 #define ORTHROS_F32 0
@@ -160,8 +169,8 @@ int orthros_swa_prefill(const void *q_pre, const float *alpha,
  *   o_x          [dev] [B, T_out, Hq, D] dtype, written
  *   ws, ws_bytes [dev] scratch of at least orthros_workspace_bytes(
  *                ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D, T_out, T_in+T_out,
- *                head_map) bytes (may be NULL when that size is 0); contents
- *                on entry are ignored and left undefined.
+ *                head_map) bytes (may be NULL when that size is 0); its
+ *                leading counters zero (see the conventions above).
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
  */
 int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
@@ -202,7 +211,7 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
  *   W                  base window, >= 1
  *   ws, ws_bytes       scratch of orthros_workspace_bytes(
  *                      ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after,
- *                      head_map)
+ *                      head_map), its leading counters zero
  * Errors: EINVAL, EUNSUPPORTED, ECAPACITY (max_len_after > cap), EWORKSPACE,
  * EHIP.
  */
@@ -228,13 +237,17 @@ int orthros_decode_pair(const void *q_pre, const void *qx_pre,
  * Sizes whose scratch (orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, ...,
  * head_map)) exceeds ORTHROS_NOALLOC_SCRATCH_BYTES are rejected with
  * ORTHROS_EWORKSPACE before anything is launched; 64 MiB covers, e.g.,
- * B = 64 sequences of 32/8 heads up to about 60K cached keys. Every call on
- * a device shares that device's array: calls that overlap in time on one
- * device (different streams, no ordering) race and give wrong results. The
- * array needs no initial contents (every byte a call reads it wrote first).
+ * B = 64 sequences of 32/8 heads up to about 60K cached keys. The array's
+ * first ORTHROS_NOALLOC_COUNTER_BYTES hold the arrival counters at a fixed
+ * place (zero when the library is loaded, left zero by every call), so
+ * sizes whose counters (orthros_workspace_counter_bytes) exceed that are
+ * rejected too; the partials follow them. Every call on a device shares
+ * that device's array: calls that overlap in time on one device (different
+ * streams, no ordering) race and give wrong results.
  * Arguments, results and errors otherwise as orthros_decode_pair.
  */
 #define ORTHROS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define ORTHROS_NOALLOC_COUNTER_BYTES ((size_t)64 << 10)
 int orthros_decode_pair_noalloc(const void *q_pre, const void *qx_pre,
                                 const float *alpha, const float *beta,
                                 const float *alpha_x, const float *beta_x,
@@ -296,7 +309,7 @@ int orthros_kv_append_paged(void *k_pool, void *v_pool, int64_t n_pages,
  *                  1 <= max_len_after <= max_pages * page_size
  *   ws, ws_bytes   scratch of orthros_workspace_bytes(
  *                  ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1, max_len_after,
- *                  head_map)
+ *                  head_map), its leading counters zero
  * Other arguments as orthros_decode_pair.
  * Errors: EINVAL, EUNSUPPORTED (dtype or D), ECAPACITY, EWORKSPACE, EHIP.
  */
@@ -392,7 +405,9 @@ size_t orthros_backward_workspace_bytes(int B, int T, int T_out, int Hq,
  *   cache_len   [dev] int32[B], set to T (whatever it held before)
  *   y           [dev] [B, T + T_out, d_model] bf16, written
  *   ws, ws_bytes [dev] scratch of orthros_layer_workspace_bytes(...) bytes
- *               (intermediates of one batch entry plus GEMM workspace)
+ *               (intermediates of one batch entry plus GEMM workspace);
+ *               contents on entry are ignored (the call zeroes the counters
+ *               its cross-attention needs)
  * 1 <= T, 0 <= T_out <= T, cap >= T, W >= 1, Hq a multiple of Hkv.
  * Errors: EINVAL, EUNSUPPORTED (D), EWORKSPACE, EHIP (also a failing
  * hipBLASLt call). The first call on a device creates that device's
@@ -425,6 +440,19 @@ size_t orthros_layer_workspace_bytes(int B, int T, int T_out, int d_model,
 size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
                                int T_out, int64_t max_len,
                                const int32_t *head_map);
+
+/*
+ * Leading bytes of that workspace holding the arrival counters, which must
+ * be zero when a call starts (every call leaves them zero). The split-KV
+ * calls run as one launch: each workgroup writes its partial result, then
+ * counts itself in, and the last to arrive for a (batch entry, head group)
+ * combines the partials (in a decode step the last to leave a batch entry
+ * also advances its length). Depends on B and the head grouping only.
+ * Arguments and zero returns as orthros_workspace_bytes; pure host function.
+ */
+size_t orthros_workspace_counter_bytes(int op, int B, int Hq, int Hkv, int D,
+                                       int T_out, int64_t max_len,
+                                       const int32_t *head_map);
 
 /* Static description of a status code. */
 const char *orthros_strerror(int code);

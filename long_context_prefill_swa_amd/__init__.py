@@ -23,6 +23,7 @@ __all__ = [
     "orthros_decode_pair", "orthros_decode_pair_noalloc",
     "orthros_kv_append_paged", "ORTHROS_NOALLOC_SCRATCH_BYTES",
     "orthros_decode_pair_paged", "orthros_workspace_bytes",
+    "orthros_workspace_counter_bytes", "ORTHROS_NOALLOC_COUNTER_BYTES",
     "orthros_check_device_errors", "orthros_abi_version",
     "orthros_strerror", "orthros_last_error", "workspace",
 ]
@@ -32,6 +33,7 @@ ORTHROS_BF16 = 1
 ORTHROS_OP_GLOBAL_XATTN = 1
 ORTHROS_OP_DECODE_PAIR = 2
 ORTHROS_NOALLOC_SCRATCH_BYTES = 64 << 20
+ORTHROS_NOALLOC_COUNTER_BYTES = 64 << 10
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "liborthros.so")
@@ -83,6 +85,9 @@ def lib():
     L.orthros_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i64,
                                           vp]
     L.orthros_workspace_bytes.restype = sz
+    L.orthros_workspace_counter_bytes.argtypes = [i32, i32, i32, i32, i32,
+                                                  i32, i64, vp]
+    L.orthros_workspace_counter_bytes.restype = sz
     L.orthros_strerror.argtypes = [i32]
     L.orthros_strerror.restype = ctypes.c_char_p
     L.orthros_last_error.argtypes = []
@@ -156,15 +161,32 @@ def _stream(stream, like):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _scratch(nbytes, device, stream):
-    """Scratch allocated here for one call. The caching allocator ties a
-    tensor to the stream current at allocation; when the call runs on
-    another stream, the block must not be handed out again until that
-    stream's work is done, hence record_stream."""
-    ws = workspace(nbytes, device)
-    if stream is not None:
-        ws.record_stream(stream)
-    return ws
+def _scratch(nbytes, device, stream, zero_bytes=0):
+    """Scratch allocated here for one call, its first zero_bytes cleared.
+    Both happen on the stream the call runs on: the clearing is then ordered
+    before the call, and the caching allocator, which ties a block to the
+    stream current at allocation, does not hand the block out again before
+    that stream's work is done."""
+    def make():
+        ws = torch.empty(max(int(nbytes), 16), dtype=torch.uint8,
+                         device=device)
+        if zero_bytes:
+            ws[:int(zero_bytes)].zero_()
+        return ws
+    if stream is None:
+        return make()
+    with torch.cuda.stream(stream):
+        return make()
+
+
+def _split_scratch(op, B, Hq, Hkv, D, T_out, max_len, head_map, device,
+                   stream):
+    """Per-call workspace of a split-KV call (None when it needs none)."""
+    need = orthros_workspace_bytes(op, B, Hq, Hkv, D, T_out, max_len, head_map)
+    if not need:
+        return None
+    return _scratch(need, device, stream, orthros_workspace_counter_bytes(
+        op, B, Hq, Hkv, D, T_out, max_len, head_map))
 
 
 def _map(head_map, Hq=None):
@@ -196,9 +218,20 @@ def orthros_workspace_bytes(op, B, Hq, Hkv, D, T_out, max_len, head_map=None):
                                              int(max_len), hm))
 
 
+def orthros_workspace_counter_bytes(op, B, Hq, Hkv, D, T_out, max_len,
+                                    head_map=None):
+    hm, _keep = _map(head_map, Hq)
+    return int(lib().orthros_workspace_counter_bytes(op, B, Hq, Hkv, D, T_out,
+                                                     int(max_len), hm))
+
+
 def workspace(nbytes, device):
-    """Caller-owned scratch buffer (16-byte aligned) for the split-KV calls."""
-    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+    """Caller-owned workspace (16-byte aligned) for the split-KV calls,
+    zero-filled on the current stream: its leading arrival counters must be
+    zero before the first call, and every call leaves them zero. Zero it
+    again (ws.zero_()) before a call with more (batch entry, head group)
+    pairs than the calls it has served."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 def orthros_kv_append(k_cache, v_cache, cache_len, k_new, v_new, stream=None):
@@ -245,9 +278,8 @@ def orthros_global_xattn(qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x, T_in,
     dt = qx_pre.dtype
     ax_p, bx_p = _vecs(Hq * D, (alpha_x, "alpha_x"), (beta_x, "beta_x"))
     if ws is None:
-        need = orthros_workspace_bytes(ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D,
-                                       T_out, int(T_in) + T_out, head_map)
-        ws = _scratch(need, qx_pre.device, stream) if need else None
+        ws = _split_scratch(ORTHROS_OP_GLOBAL_XATTN, B, Hq, Hkv, D, T_out,
+                            int(T_in) + T_out, head_map, qx_pre.device, stream)
     hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_global_xattn(
         _dev(qx_pre, "qx_pre", dt), ax_p, bx_p, _dev(k_cache, "k_cache", dt),
@@ -274,9 +306,8 @@ def orthros_decode_pair(q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
                 (alpha_x, "alpha_x"), (beta_x, "beta_x"))
     cl_p = _dev(cache_len, "cache_len", torch.int32)
     if ws is None:
-        need = orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D,
-                                       1, int(max_len_after), head_map)
-        ws = _scratch(need, q_pre.device, stream) if need else None
+        ws = _split_scratch(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1,
+                            int(max_len_after), head_map, q_pre.device, stream)
     hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_decode_pair(
         _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt), *aff,
@@ -371,9 +402,8 @@ def orthros_decode_pair_paged(q_pre, qx_pre, alpha, beta, alpha_x, beta_x,
                 (alpha_x, "alpha_x"), (beta_x, "beta_x"))
     cl_p = _dev(cache_len, "cache_len", torch.int32)
     if ws is None:
-        need = orthros_workspace_bytes(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D,
-                                       1, int(max_len_after), head_map)
-        ws = _scratch(need, q_pre.device, stream) if need else None
+        ws = _split_scratch(ORTHROS_OP_DECODE_PAIR, B, Hq, Hkv, D, 1,
+                            int(max_len_after), head_map, q_pre.device, stream)
     hm, _keep = _map(head_map, Hq)
     _check(lib().orthros_decode_pair_paged(
         _dev(q_pre, "q_pre", dt), _dev(qx_pre, "qx_pre", dt), *aff,

@@ -20,6 +20,7 @@ PROBE_SRC = "clock_probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kv_append.hip", "rowwise.hip", "splitkv_mfma.hip", "splitkv_plan.cpp",
+           "noalloc_scratch.hip",
            "band_mfma.hip", "band_roll.hip", "band_persist.hip",
            "band_bwd.hip", "orthros_api.cpp", "gemm.cpp", "layer.cpp"]
 

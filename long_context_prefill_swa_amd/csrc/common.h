@@ -183,7 +183,9 @@ struct SplitKVArgs {
   int n_chunks;
   float *ws;                 // partials: (max, sum) pairs, then outputs
   int64_t ws_acc_offset;     // float offset of the unnormalised outputs
-  int32_t *ws_len;           // decode: per-batch old length or -1
+  int32_t *counters;         // [B * n_groups] arrivals per (batch, group),
+                             // then [B] (decode) per batch entry; zero at
+                             // the start of a call, left zero at its end
   int *flag;
   // Paged cache (block_table != nullptr): k_cache / v_cache are pools of
   // n_pages pages [n_pages, n_kv_heads, page_size, D]; key i of batch entry
@@ -195,8 +197,12 @@ struct SplitKVArgs {
   int64_t n_pages;
 };
 int splitkv_rows(int n_streams, int n_pos, int gsize);
+size_t splitkv_counter_bytes(int B, int n_groups);
+// Device address, on the current device, of the no-allocation decode pair's
+// static scratch array (looked up on the first call on that device).
+hipError_t noalloc_scratch_ptr(void **out);
 size_t splitkv_ws_bytes(int B, int n_groups, int rows, int n_chunks, int D);
-int splitkv_pick_chunk(int B, int n_groups, int64_t max_len);
+int splitkv_pick_chunk(int B, int n_groups, int64_t max_len, int max_chunk);
 hipError_t launch_splitkv(const SplitKVArgs &a, const HeadGroups &groups,
                           hipStream_t stream);
 

@@ -32,7 +32,8 @@ constexpr size_t kGemmWorkspace = size_t(64) << 20;
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 struct LayerWs {
-  size_t q_all, k, v, o_cat, xattn_ws, xattn_bytes, gemm_ws, total;
+  size_t q_all, k, v, o_cat, xattn_ws, xattn_bytes, xattn_counter_bytes,
+      gemm_ws, total;
 };
 
 // Workspace layout, reused by the batch entries one after the other.
@@ -50,6 +51,10 @@ bool layer_ws(int T, int T_out, int Hq, int Hkv, int D, LayerWs *w) {
   w->xattn_bytes = T_out > 0 ? orthros_workspace_bytes(ORTHROS_OP_GLOBAL_XATTN, 1, Hq,
                                                        Hkv, D, T_out, T, nullptr)
                              : 0;
+  w->xattn_counter_bytes = T_out > 0 ? orthros_workspace_counter_bytes(
+                                           ORTHROS_OP_GLOBAL_XATTN, 1, Hq, Hkv,
+                                           D, T_out, T, nullptr)
+                                     : 0;
   w->xattn_ws = off;
   off += align256(w->xattn_bytes);
   w->gemm_ws = off;
@@ -58,7 +63,14 @@ bool layer_ws(int T, int T_out, int Hq, int Hkv, int D, LayerWs *w) {
   return true;
 }
 
-__global__ void set_len_kernel(int32_t *p, int32_t v) { *p = v; }
+// Sets one cache length and zeroes the n int32 arrival counters at the start
+// of the cross-attention workspace (the split-KV kernel expects them zero;
+// the layer workspace may hold anything on entry). One block of 64 threads.
+__global__ void set_len_kernel(int32_t *len, int32_t v, int32_t *counters,
+                               int n) {
+  if (threadIdx.x == 0) *len = v;
+  for (int i = threadIdx.x; i < n; i += 64) counters[i] = 0;
+}
 
 int fail_msg(int code, const char *fmt, long long a = 0, long long b = 0) {
   char buf[256];
@@ -132,7 +144,9 @@ extern "C" int orthros_layer_forward(
                   kGemmWorkspace, st, msg, sizeof(msg)))
       return api_error(ORTHROS_EHIP, msg);
     // the cache of this sequence is filled from row 0
-    hipLaunchKernelGGL(set_len_kernel, dim3(1), dim3(1), 0, st, cache_len + b, 0);
+    hipLaunchKernelGGL(set_len_kernel, dim3(1), dim3(64), 0, st, cache_len + b,
+                       0, (int32_t *)(base + lw.xattn_ws),
+                       (int)(lw.xattn_counter_bytes / 4));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail_msg(ORTHROS_EHIP, "length reset launch failed");
     int rc = orthros_kv_append(kc, vc, cache_len + b, kp, vp, 1, T, Hkv, D, cap,

@@ -6,7 +6,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 
 #include "../../include/orthros.h"
 #include "common.h"
@@ -142,29 +141,64 @@ struct SplitPlan {
   size_t ws_bytes = 0;
 };
 
+// Chunks of at most 4096 keys on a contiguous cache, 2048 on a paged one (a
+// chunk spans at most 64 pages). A decode step's workspace is sized for the
+// paged plan, which never needs less than the contiguous one: the chunk the
+// contiguous plan picks is at least as large, so it has no more chunks.
+constexpr int kChunkContiguous = 4096;
+constexpr int kChunkPaged = 2048;
+
 SplitPlan plan_split(int B, int n_streams, int n_pos, const HeadGroups &g,
-                     int D, int64_t max_len) {
+                     int D, int64_t max_len, int max_chunk) {
   SplitPlan p;
   p.rows = splitkv_rows(n_streams, n_pos, g.gsize);
   // The split kernel addresses one (batch, KV head) slab of the cache with
   // 32-bit byte offsets: max_len rows of 256 bytes must stay below 4 GiB.
   if (D != 128 || p.rows > 16 || max_len > (int64_t)(UINT32_MAX / 256)) return p;
   p.use = true;
-  p.chunk = splitkv_pick_chunk(B, g.n_groups, max_len);
+  p.chunk = splitkv_pick_chunk(B, g.n_groups, max_len, max_chunk);
   p.n_chunks = (int)((max_len + p.chunk - 1) / p.chunk);
   p.ws_bytes = splitkv_ws_bytes(B, g.n_groups, p.rows, p.n_chunks, D);
   return p;
 }
 
+// The counters take the first counter_region bytes of ws (at least
+// splitkv_counter_bytes), the partials the rest.
 void fill_ws(SplitKVArgs *a, void *ws, const SplitPlan &p, int B,
-             int n_groups) {
-  const size_t len_bytes = ((size_t)B * 4 + 255) / 256 * 256;
-  a->ws_len = (int32_t *)ws;
-  a->ws = (float *)((char *)ws + len_bytes);
+             int n_groups, size_t counter_region) {
+  a->counters = (int32_t *)ws;
+  a->ws = (float *)((char *)ws + counter_region);
   const int64_t parts = (int64_t)B * n_groups * p.n_chunks * p.rows;
   a->ws_acc_offset = (parts * 2 + 63) / 64 * 64;
   a->chunk = p.chunk;
   a->n_chunks = p.n_chunks;
+}
+
+// The split plan of a workspace query; false when the call needs no
+// workspace (unknown op, invalid sizes or map, or no split-KV launch).
+// A pure query: the caller's last error message is left as it was.
+bool query_plan(int op, int B, int Hq, int Hkv, int D, int T_out,
+                int64_t max_len, const int32_t *head_map, SplitPlan *p,
+                HeadGroups *g) {
+  if (B < 1 || T_out < 1 || max_len < 1 || D < 1 || D > ORTHROS_MAX_D)
+    return false;
+  if (Hq < 1 || Hkv < 1 || Hq > ORTHROS_MAX_HEADS || Hkv > ORTHROS_MAX_HEADS)
+    return false;
+  // The same head grouping the calls build from (head_map, Hq, Hkv): the
+  // number of groups and the group width size the partials.
+  HeadMap map;
+  char saved[sizeof(g_msg)];
+  memcpy(saved, g_msg, sizeof(g_msg));
+  const int rc = build_maps(head_map, Hq, Hkv, &map, g);
+  memcpy(g_msg, saved, sizeof(g_msg));
+  if (rc != ORTHROS_OK) return false;
+  if (op == ORTHROS_OP_GLOBAL_XATTN)
+    *p = plan_split(B, 1, T_out, *g, D, max_len, kChunkContiguous);
+  else if (op == ORTHROS_OP_DECODE_PAIR)
+    *p = plan_split(B, 2, 1, *g, D, max_len, kChunkPaged);
+  else
+    return false;
+  return p->use;
 }
 
 }  // namespace
@@ -198,28 +232,21 @@ const char *orthros_last_error(void) { return g_msg; }
 size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
                                int T_out, int64_t max_len,
                                const int32_t *head_map) {
-  if (B < 1 || T_out < 1 || max_len < 1 || D < 1 || D > ORTHROS_MAX_D)
-    return 0;
-  if (Hq < 1 || Hkv < 1 || Hq > ORTHROS_MAX_HEADS || Hkv > ORTHROS_MAX_HEADS)
-    return 0;
-  // The same head grouping the calls build from (head_map, Hq, Hkv): the
-  // number of groups and the group width size the partials.
-  // A pure query: the caller's last error message is left as it was.
-  HeadMap map;
-  HeadGroups g;
-  char saved[sizeof(g_msg)];
-  memcpy(saved, g_msg, sizeof(g_msg));
-  const int rc = build_maps(head_map, Hq, Hkv, &map, &g);
-  memcpy(g_msg, saved, sizeof(g_msg));
-  if (rc != ORTHROS_OK) return 0;
   SplitPlan p;
-  if (op == ORTHROS_OP_GLOBAL_XATTN)
-    p = plan_split(B, 1, T_out, g, D, max_len);
-  else if (op == ORTHROS_OP_DECODE_PAIR)
-    p = plan_split(B, 2, 1, g, D, max_len);
-  else
-    return 0;
-  return p.use ? p.ws_bytes : 0;
+  HeadGroups g;
+  return query_plan(op, B, Hq, Hkv, D, T_out, max_len, head_map, &p, &g)
+             ? p.ws_bytes
+             : 0;
+}
+
+size_t orthros_workspace_counter_bytes(int op, int B, int Hq, int Hkv, int D,
+                                       int T_out, int64_t max_len,
+                                       const int32_t *head_map) {
+  SplitPlan p;
+  HeadGroups g;
+  return query_plan(op, B, Hq, Hkv, D, T_out, max_len, head_map, &p, &g)
+             ? splitkv_counter_bytes(B, g.n_groups)
+             : 0;
 }
 
 int orthros_kv_append(void *k_cache, void *v_cache, int32_t *cache_len,
@@ -327,7 +354,8 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
   hipError_t e;
   const bool mfma =
       mfma_eligible(dtype, D, T, {qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x});
-  const SplitPlan plan = plan_split(B, 1, T_out, groups, D, T);
+  const SplitPlan plan =
+      plan_split(B, 1, T_out, groups, D, T, kChunkContiguous);
   if (mfma && plan.use) {
     if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))
       return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
@@ -349,7 +377,8 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
     a.k_cache = const_cast<void *>(k_cache);
     a.v_cache = const_cast<void *>(v_cache);
     a.max_len = T;
-    fill_ws(&a, ws, plan, B, groups.n_groups);
+    fill_ws(&a, ws, plan, B, groups.n_groups,
+            splitkv_counter_bytes(B, groups.n_groups));
     e = device_flag_ptr(&a.flag);
     if (e != hipSuccess) return hip_fail("device flag", e);
     e = launch_splitkv(a, groups, as_stream(stream));
@@ -376,36 +405,8 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
 
 namespace {
 
-// ---- scratch of the no-allocation decode pair -------------------------------
-// A static device array, one copy per device the library runs on, alive until
-// the process ends. Host code never uses the array's name as an address (in
-// host code it is a stand-in, not a device pointer): the device address is
-// looked up once per device with hipGetSymbolAddress and kept.
 constexpr size_t kScratchBytes = ORTHROS_NOALLOC_SCRATCH_BYTES;
-__device__ __align__(256) unsigned char scratch[kScratchBytes];
-
-constexpr int kMaxDevices = 64;
-std::mutex g_scratch_mu;
-void *g_scratch_ptr[kMaxDevices] = {nullptr};
-
-// Device address of `scratch` on the current device (looked up on the first
-// call on that device, with that device current).
-hipError_t scratch_ptr(void **out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  if (!g_scratch_ptr[dev]) {
-    void *p = nullptr;
-    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    if (e != hipSuccess) return e;
-    if (!p) return hipErrorInvalidSymbol;
-    g_scratch_ptr[dev] = p;
-  }
-  *out = g_scratch_ptr[dev];
-  return hipSuccess;
-}
+constexpr size_t kScratchCounterBytes = ORTHROS_NOALLOC_COUNTER_BYTES;
 
 // The decode pair step. With from_scratch, the split-KV partials go to the
 // static scratch array instead of the caller's ws (which is then ignored).
@@ -445,21 +446,34 @@ int decode_pair_impl(const void *q_pre, const void *qx_pre,
   const bool mfma = mfma_eligible(
       dtype, D, max_len_after, {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new, v_new,
                  k_cache, v_cache, o, o_x});
-  const SplitPlan plan = plan_split(B, 2, 1, groups, D, max_len_after);
+  // checked against the workspace query's (paged) size, launched with the
+  // contiguous plan, which fits in it
+  const size_t ws_need =
+      plan_split(B, 2, 1, groups, D, max_len_after, kChunkPaged).ws_bytes;
+  const SplitPlan plan =
+      plan_split(B, 2, 1, groups, D, max_len_after, kChunkContiguous);
   hipError_t e;
+  size_t counter_region = splitkv_counter_bytes(B, groups.n_groups);
   if (mfma && plan.use && from_scratch) {
-    if (plan.ws_bytes > kScratchBytes)
+    // The scratch array keeps its counters in a fixed leading region, so
+    // that no call's partials land where a later call with more (batch,
+    // group) pairs expects zeroed counters.
+    const size_t need = ws_need - counter_region + kScratchCounterBytes;
+    if (counter_region > kScratchCounterBytes || need > kScratchBytes)
       return fail(ORTHROS_EWORKSPACE,
-                  "these sizes need %zu bytes of scratch; the no-allocation "
-                  "decode pair holds %zu (use orthros_decode_pair with a "
-                  "workspace)", plan.ws_bytes, kScratchBytes);
-    e = scratch_ptr(&ws);
+                  "these sizes need %zu bytes of scratch (%zu of counters); "
+                  "the no-allocation decode pair holds %zu (%zu of counters; "
+                  "use orthros_decode_pair with a workspace)",
+                  ws_need, counter_region, kScratchBytes,
+                  kScratchCounterBytes);
+    e = noalloc_scratch_ptr(&ws);
     if (e != hipSuccess) return hip_fail("scratch symbol", e);
     ws_bytes = kScratchBytes;
+    counter_region = kScratchCounterBytes;
   }
-  if (mfma && plan.use && (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)))
+  if (mfma && plan.use && (!ws || ws_bytes < ws_need || !aligned16(ws)))
     return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
-                plan.ws_bytes, ws ? ws_bytes : (size_t)0);
+                ws_need, ws ? ws_bytes : (size_t)0);
   int *flag = nullptr;
   e = device_flag_ptr(&flag);
   if (e != hipSuccess) return hip_fail("device flag", e);
@@ -489,7 +503,7 @@ int decode_pair_impl(const void *q_pre, const void *qx_pre,
     a.v_new = v_new;
     a.max_len = max_len_after;
     a.flag = flag;
-    fill_ws(&a, ws, plan, B, groups.n_groups);
+    fill_ws(&a, ws, plan, B, groups.n_groups, counter_region);
     e = launch_splitkv(a, groups, st);
     if (e != hipSuccess) return hip_fail("decode_pair launch", e);
     return ORTHROS_OK;
@@ -642,7 +656,8 @@ int orthros_decode_pair_paged(const void *q_pre, const void *qx_pre,
                      {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new,
                       v_new, k_pool, v_pool, o, o_x}))
     return fail(ORTHROS_EINVAL, "tensors must be 16-byte aligned");
-  const SplitPlan plan = plan_split(B, 2, 1, groups, D, max_len_after);
+  const SplitPlan plan =
+      plan_split(B, 2, 1, groups, D, max_len_after, kChunkPaged);
   if (!plan.use)
     return fail(ORTHROS_EUNSUPPORTED, "no split plan for these sizes");
   if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))
@@ -680,7 +695,8 @@ int orthros_decode_pair_paged(const void *q_pre, const void *qx_pre,
   a.max_pages = max_pages;
   a.page_log2 = log2;
   a.n_pages = n_pages;
-  fill_ws(&a, ws, plan, B, groups.n_groups);
+  fill_ws(&a, ws, plan, B, groups.n_groups,
+          splitkv_counter_bytes(B, groups.n_groups));
   e = launch_splitkv(a, groups, as_stream(stream));
   if (e != hipSuccess) return hip_fail("decode_pair_paged launch", e);
   return ORTHROS_OK;

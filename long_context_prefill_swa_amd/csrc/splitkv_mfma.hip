@@ -31,9 +31,12 @@
 // masked, so the loop has no data-dependent branch.
 //
 // After the loop the 4 waves merge in LDS and the workgroup writes one
-// (max, sum, unnormalised output) partial per row; a second kernel combines
-// the partials of all chunks with log-sum-exp weights, normalises, writes the
-// output rows and (decode) advances the cache length.
+// (max, sum, unnormalised output) partial per row. It then counts itself in
+// at its (batch, head group): the last workgroup to arrive combines the
+// partials of all chunks with log-sum-exp weights, normalises and writes the
+// output rows. In a decode step the last group of a batch entry to finish
+// its merge then advances the cache length. One launch per call; the
+// arrival counters sit in the workspace, start at zero and are left at zero.
 #include "common.h"
 
 namespace orthros {
@@ -57,9 +60,16 @@ struct Merge {
   float m[kWaves][kMaxRows];
   float l[kWaves][kMaxRows];
 };
+// The last arriver's combination of the chunks' partials: the 8 half-wave
+// slots' running results.
+struct Combine {
+  float m[8], l[8];
+  float acc[8][D];
+};
 union SplitSmem {
   VStage st;
   Merge mg;
+  Combine cb;
 };
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
@@ -76,16 +86,146 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ int64_t row_pos(const SplitKVArgs &a, int b,
-                                           int j) {
-  return (a.cache_len ? (int64_t)a.cache_len[b] : a.pos0) + j;
-}
-
 __device__ __forceinline__ int64_t ws_part_index(const SplitKVArgs &a,
                                                  int n_groups, int rows,
                                                  int b, int gi, int c,
                                                  int r) {
   return (((int64_t)b * n_groups + gi) * a.n_chunks + c) * rows + r;
+}
+
+// The partials cross workgroups, and so compute units and XCDs, within one
+// launch. They are written and read with device-scope buffer stores and
+// loads (cache policy SC1), which go to the level of the memory hierarchy
+// all XCDs share; the writer waits for its stores to complete before it
+// counts itself in. No cache-wide write-back or invalidation (what a
+// device-scope fence does) is needed: those cost microseconds per
+// workgroup. Every store and load instruction covers whole 128-byte lines
+// (a half wave moves one 512-byte row of a partial): device-scope accesses
+// are not combined in the L2, so partial lines would multiply the requests.
+constexpr int kDeviceScope = 16;  // buffer cache policy: SC1
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The partials of (batch b, group gi): (max, sum) pairs and output rows of
+// its n_chunks x rows partials, as two buffer resources (byte offsets
+// (c rows + r) x 8 and x 512).
+struct PartialView {
+  __amdgpu_buffer_rsrc_t ml, acc;
+};
+__device__ __forceinline__ PartialView partial_view(const SplitKVArgs &a,
+                                                    int n_groups, int rows,
+                                                    int b, int gi) {
+  const int64_t p0 = ((int64_t)b * n_groups + gi) * a.n_chunks * rows;
+  const int n = a.n_chunks * rows;
+  PartialView v;
+  v.ml = __builtin_amdgcn_make_buffer_rsrc(a.ws + p0 * 2, 0, n * 8,
+                                           kBufferWord3);
+  v.acc = __builtin_amdgcn_make_buffer_rsrc(
+      a.ws + a.ws_acc_offset + p0 * D, 0, n * D * 4, kBufferWord3);
+  return v;
+}
+
+// The last arriver of (batch b, group gi): every output row of the group,
+// from the partials of the chunks that hold keys of the row's range,
+// combined with log-sum-exp weights, normalised and written in bf16. Rows go
+// in passes of nr <= 8; in a pass the 8 half-wave slots split as spr =
+// 8 / nr slots per row, slot g taking row r0 + g % nr and every spr-th chunk
+// of its range from c_lo + g / nr. Lane f of a slot holds channels 4f ..
+// 4f + 3 and a running (max, sum, output); loads go out kBatch chunks at a
+// time, so a slot's chunks cost a few memory round trips. The slots of a row
+// are then combined in LDS. Called by all threads of the workgroup.
+__device__ __forceinline__ void combine_group(const SplitKVArgs &a,
+                                              const HeadGroups &groups,
+                                              Combine &cb, int b, int gi,
+                                              int64_t pos_base) {
+  constexpr int kBatch = 8;
+  const int tid = threadIdx.x;
+  const int gsize = groups.gsize;
+  const int rows = a.n_streams * a.n_pos * gsize;
+  const PartialView pv = partial_view(a, groups.n_groups, rows, b, gi);
+  const int g = tid >> 5, f = tid & 31;
+  for (int r0 = 0; r0 < rows; r0 += 8) {
+    const int nr = min(rows - r0, 8), spr = 8 / nr;
+    float M = -INFINITY, L = 0.0f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (g < nr * spr) {
+      const int r = r0 + g % nr, sub = g / nr;
+      const int s = r / (a.n_pos * gsize);
+      const int64_t t = pos_base + (r / gsize) % a.n_pos;
+      const int Ws = a.W[s];
+      const int64_t lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
+      const int c_lo = (int)(lo / a.chunk), c_hi = (int)(t / a.chunk);
+      for (int c0 = c_lo + sub; c0 <= c_hi; c0 += kBatch * spr) {
+        f32x2 mlv[kBatch];
+        f32x4 u[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          // past the range: reload the last chunk, weight it out below
+          const int cc = min(c0 + k * spr, c_hi);
+          const int pi = cc * rows + r;
+          mlv[k] = __builtin_bit_cast(
+              f32x2, __builtin_amdgcn_raw_buffer_load_b64(pv.ml, pi * 8, 0,
+                                                          kDeviceScope));
+          u[k] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         pv.acc, pi * (D * 4) + f * 16, 0, kDeviceScope));
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+          const float mc = c0 + k * spr <= c_hi ? mlv[k].x : -INFINITY;
+          if (mc != -INFINITY) {  // a chunk with keys in this row's range
+            const float Mn = fmaxf(M, mc);
+            const float fo = exp2f(M - Mn), fn = exp2f(mc - Mn);
+            L = L * fo + mlv[k].y * fn;
+            o = o * fo + u[k] * fn;
+            M = Mn;
+          }
+        }
+      }
+    }
+    __syncthreads();  // the previous pass's readers of cb are done
+    if (f == 0) {
+      cb.m[g] = M;
+      cb.l[g] = L;
+    }
+    *(f32x4 *)&cb.acc[g][4 * f] = o;
+    __syncthreads();
+    const int j = tid >> 5;  // row r0 + j, channels 4f .. 4f + 3
+    if (j < nr) {
+      const int r = r0 + j;
+      const int h = groups.q[gi][r % gsize];
+      if (h >= 0) {  // a padded head slot has no output row
+        float Mx = -INFINITY;
+        for (int q = 0; q < spr; ++q) Mx = fmaxf(Mx, cb.m[j + q * nr]);
+        float Lx = 0.0f;
+        f32x4 out = {0.f, 0.f, 0.f, 0.f};
+        if (Mx != -INFINITY) {
+          for (int q = 0; q < spr; ++q) {
+            const int gq = j + q * nr;
+            const float w = exp2f(cb.m[gq] - Mx);  // 0 for an empty slot
+            Lx += w * cb.l[gq];
+            out += w * *(const f32x4 *)&cb.acc[gq][4 * f];
+          }
+        }
+        const float inv = Lx > 0.0f ? 1.0f / Lx : 0.0f;
+        const int s = r / (a.n_pos * gsize);
+        const int jp = (r / gsize) % a.n_pos;
+        uint16_t *dst = (uint16_t *)a.o[s] +
+                        (((int64_t)b * a.n_pos + jp) * a.Hq + h) * D + 4 * f;
+        uint32_t w2[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t lo16 =
+              __builtin_bit_cast(uint16_t, (__bf16)(out[2 * e] * inv));
+          const uint32_t hi16 =
+              __builtin_bit_cast(uint16_t, (__bf16)(out[2 * e + 1] * inv));
+          w2[e] = lo16 | (hi16 << 16);
+        }
+        *(uint2 *)dst = make_uint2(w2[0], w2[1]);
+      }
+    }
+  }
 }
 
 // Registers of one 32-key slice: K in MFMA operand layout (lane (col, g4)
@@ -119,15 +259,45 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   if (a.cache_len) {
     n_old = a.cache_len[b];
     const bool ok = n_old >= 0 && n_old + 1 <= a.max_len && n_old + 1 <= a.cap;
-    if (c == 0 && gi == 0 && tid == 0) {
-      a.ws_len[b] = ok ? (int32_t)n_old : -1;
-      if (!ok) atomicOr(a.flag, 1);
+    if (!ok) {
+      // skipped (the length is left unchanged): chunk 0 of each group
+      // writes the group's output rows as zeros
+      if (c == 0) {
+        if (gi == 0 && tid == 0) atomicOr(a.flag, 1);
+        const int r = tid >> 4, d0 = (tid & 15) * 8;
+        if (r < rows) {
+          const int hq = groups.q[gi][r % gsize];
+          if (hq >= 0) {
+            uint16_t *dst =
+                (uint16_t *)a.o[r / (a.n_pos * gsize)] +
+                (((int64_t)b * a.n_pos + (r / gsize) % a.n_pos) * a.Hq + hq) * D +
+                d0;
+            *(uint4 *)dst = make_uint4(0, 0, 0, 0);
+          }
+        }
+      }
+      return;
     }
-    if (!ok) return;
   }
-  const int64_t hi_max = row_pos(a, b, a.n_pos - 1);
+  // Decode: each workgroup of batch entry b counts itself out once it is
+  // done with the entry's length; the last one out advances the length
+  // (every other workgroup of the entry has read it by then).
+  auto leave = [&]() {
+    if (a.cache_len && tid == 0) {
+      int32_t *bc = a.counters + (int64_t)a.B * groups.n_groups + b;
+      if (atomicAdd(bc, 1) == (int)(gridDim.x * gridDim.y) - 1) {
+        atomicExch(bc, 0);
+        ((int32_t *)a.cache_len)[b] = (int32_t)(n_old + 1);
+      }
+    }
+  };
+  const int64_t pos_base = a.cache_len ? n_old : a.pos0;  // row 0's position
+  const int64_t hi_max = pos_base + a.n_pos - 1;
   const int64_t k_begin = (int64_t)c * a.chunk;
-  if (k_begin > hi_max) return;
+  if (k_begin > hi_max) {
+    leave();
+    return;
+  }
   // keys of this workgroup: [k_begin, k_stop)
   const int64_t k_stop = min(k_begin + (int64_t)a.chunk, hi_max + 1);
   const int n_steps = (int)((k_stop - k_begin + kStepKeys - 1) / kStepKeys);
@@ -141,7 +311,7 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   }
   int64_t r_lo = 1, r_hi = 0;  // empty unless the row is active
   if (row_h >= 0) {
-    const int64_t t = row_pos(a, b, row_j);
+    const int64_t t = pos_base + row_j;
     const int Ws = row_s ? a.W[1] : a.W[0];
     r_lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
     r_hi = min(t, k_stop - 1);
@@ -198,8 +368,7 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
       uint4 *dst = (uint4 *)((lane < 16) ? kd : vd) + part;
       *dst = *src;
     }
-    __threadfence();
-    __syncthreads();
+    __syncthreads();  // workgroup scope: only this workgroup reads the row
   }
   const uint32_t slab_bytes = (uint32_t)(k_stop * D * 2);
   const __amdgpu_buffer_rsrc_t rk =
@@ -379,150 +548,61 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
       sm.mg.acc[w][col][16 * dt + 4 * g4 + i] = acc[dt][i];
   __syncthreads();
 
-  const int r = tid >> 4;          // 16 rows x 16 threads
-  const int d0 = (tid & 15) * 8;   // 8 channels each
-  if (r < rows) {
-    float M = -INFINITY;
+  // Rows r = tid / 32 (+ 8): lane tid % 32 of a half wave combines the 4
+  // waves for channels 4 (tid % 32) .. + 3 and stores them (a whole 512-byte
+  // row per half wave); lane 0 also stores the row's (max, sum).
+  {
+    const PartialView pv = partial_view(a, groups.n_groups, rows, b, gi);
+    const int f = tid & 31;
+    for (int r = tid >> 5; r < rows; r += 8) {
+      float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.mg.m[ww][r]);
-    float L = 0.0f, o8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (M != -INFINITY) {
+      for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm.mg.m[ww][r]);
+      float L = 0.0f;
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) {
-        const float f = exp2f(sm.mg.m[ww][r] - M);  // 0 for an empty wave
-        L += f * sm.mg.l[ww][r];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o8[e] += f * sm.mg.acc[ww][r][d0 + e];
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float fw = exp2f(sm.mg.m[ww][r] - M);  // 0 for an empty wave
+          L += fw * sm.mg.l[ww][r];
+          o += fw * *(const f32x4 *)&sm.mg.acc[ww][r][4 * f];
+        }
       }
+      const int pi = c * rows + r;
+      if (f == 0)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2, f32x2{M, L}), pv.ml, pi * 8, 0,
+            kDeviceScope);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o),
+                                             pv.acc, pi * (D * 4) + f * 16, 0,
+                                             kDeviceScope);
     }
-    const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, c, r);
-    float *ml = a.ws + pi * 2;
-    float *pacc = a.ws + (int64_t)a.ws_acc_offset + pi * D + d0;
-    if (d0 == 0) {
-      ml[0] = M;
-      ml[1] = L;
-    }
-    *(float4 *)pacc = make_float4(o8[0], o8[1], o8[2], o8[3]);
-    *(float4 *)(pacc + 4) = make_float4(o8[4], o8[5], o8[6], o8[7]);
   }
-}
 
-// One workgroup per (row, head group, batch), LANES chunk lanes of
-// 256 / LANES threads. Thread (q, part): chunks c_lo + q, c_lo + q + LANES,
-// ... and channels CH part .. CH part + CH - 1 (CH = D LANES / 256). Every
-// load of a chunk is issued before its maximum is tested, so a row over up
-// to LANES chunks costs one memory round trip; the lanes are then combined
-// in LDS. 64 lanes serve rows over more than 32 chunks (a long prompt's
-// output row); 16 lanes, with a quarter of the LDS and so more resident
-// workgroups, serve the decode step's rows over a few.
-template <int LANES>
-__global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
-                                                            HeadGroups groups) {
-  constexpr int kParts = 256 / LANES, CH = D / kParts;
-  __shared__ float sm_m[LANES], sm_l[LANES], sm_f[LANES];
-  __shared__ float sm_sum;
-  __shared__ float sm_acc[LANES][D + 4];
-  const int r = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int gsize = groups.gsize;
-  const int rows = a.n_streams * a.n_pos * gsize;
-  const int s = r / (a.n_pos * gsize);
-  const int j = (r / gsize) % a.n_pos;
-  const int h = groups.q[gi][r % gsize];
-  int64_t n_old = 0;
-  bool ok = true;
-  if (a.cache_len) {
-    n_old = a.ws_len[b];
-    ok = n_old >= 0;
-  }
-  // Decode: the cache now holds n_old + 1 rows for this batch entry. Every
-  // split workgroup has finished reading (kernel boundary), and the merge
-  // reads the old length from the workspace, so this write races with none.
-  // Row 0 of group 0 always exists (its first query head).
-  if (a.cache_len && ok && r == 0 && gi == 0 && tid == 0)
-    ((int32_t *)a.cache_len)[b] = (int32_t)(n_old + 1);
-  if (h < 0) return;
-
-  const int q = tid / kParts, part = tid % kParts, d0 = CH * part;
-  float M = -INFINITY, L = 0.0f;
-  f32x4 o[CH / 4];
-#pragma unroll
-  for (int k = 0; k < CH / 4; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int64_t t = (a.cache_len ? n_old : a.pos0) + j;
-  int c_lo = 0, c_hi = -1;
-  if (ok) {
-    const int Ws = a.W[s];
-    const int64_t lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
-    c_lo = (int)(lo / a.chunk);
-    c_hi = (int)(t / a.chunk);
-  }
-  for (int cc = c_lo + q; cc <= c_hi; cc += LANES) {
-    const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, cc, r);
-    const float mc = a.ws[pi * 2];
-    const float lc = a.ws[pi * 2 + 1];
-    const f32x4 *pacc =
-        (const f32x4 *)(a.ws + (int64_t)a.ws_acc_offset + pi * D + d0);
-    f32x4 u[CH / 4];
-#pragma unroll
-    for (int k = 0; k < CH / 4; ++k) u[k] = pacc[k];
-    if (mc != -INFINITY) {  // a chunk with keys in this row's range
-      const float Mn = fmaxf(M, mc);
-      const float fo = exp2f(M - Mn), fn = exp2f(mc - Mn);
-      L = L * fo + lc * fn;
-#pragma unroll
-      for (int k = 0; k < CH / 4; ++k) o[k] = o[k] * fo + u[k] * fn;
-      M = Mn;
-    }
-  }
-  if (part == 0) {
-    sm_m[q] = M;
-    sm_l[q] = L;
-  }
-#pragma unroll
-  for (int k = 0; k < CH / 4; ++k) *(f32x4 *)&sm_acc[q][d0 + 4 * k] = o[k];
+  // ---- arrival; the last workgroup of (batch, group) merges ---------------
+  // Chunks with work for this batch entry: those starting at or before its
+  // last position (the others returned above and do not arrive). Every
+  // thread's device-scope partial stores have completed before thread 0
+  // counts the workgroup in, so the last arriver's device-scope loads see
+  // every chunk's partials.
+  const int used = (int)(hi_max / a.chunk) + 1;
+  __shared__ int last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partials are out
   __syncthreads();
-  if (tid < LANES) {
-    // the first LANES threads: the row maximum over the lanes, each lane's
-    // weight, and the sum (xor shuffles within the LANES-wide group)
-    const float mq = sm_m[tid];
-    float Mx = mq;
-#pragma unroll
-    for (int sh = LANES / 2; sh >= 1; sh >>= 1)
-      Mx = fmaxf(Mx, __shfl_xor(Mx, sh, 64));
-    const float f = (mq == -INFINITY) ? 0.0f : exp2f(mq - Mx);
-    sm_f[tid] = f;
-    float lsum = f * sm_l[tid];
-#pragma unroll
-    for (int sh = LANES / 2; sh >= 1; sh >>= 1) lsum += __shfl_xor(lsum, sh, 64);
-    if (tid == 0) sm_sum = lsum;
+  if (tid == 0) {
+    int32_t *cnt = a.counters + (int64_t)b * groups.n_groups + gi;
+    last = atomicAdd(cnt, 1) == used - 1;
+    if (last) atomicExch(cnt, 0);  // no other arrival is left in this call
   }
   __syncthreads();
-  if (tid < D / 2) {
-    // thread tid: channels 2 tid, 2 tid + 1
-    float out0 = 0.0f, out1 = 0.0f;
-#pragma unroll 8
-    for (int qq = 0; qq < LANES; ++qq) {
-      const float f = sm_f[qq];
-      const float2 v = *(const float2 *)&sm_acc[qq][2 * tid];
-      out0 += f * v.x;
-      out1 += f * v.y;
-    }
-    const float Lx = sm_sum;
-    const float inv = Lx > 0.0f ? 1.0f / Lx : 0.0f;
-    const uint32_t lo16 = __builtin_bit_cast(uint16_t, (__bf16)(out0 * inv));
-    const uint32_t hi16 = __builtin_bit_cast(uint16_t, (__bf16)(out1 * inv));
-    uint16_t *dst = (uint16_t *)a.o[s] +
-                    (((int64_t)b * a.n_pos + j) * a.Hq + h) * D + 2 * tid;
-    *(uint32_t *)dst = lo16 | (hi16 << 16);
-  }
+  if (last) combine_group(a, groups, sm.cb, b, gi, pos_base);
+  leave();
 }
 
 }  // namespace
 
-hipError_t launch_splitkv(const SplitKVArgs &a_in, const HeadGroups &groups,
+hipError_t launch_splitkv(const SplitKVArgs &a, const HeadGroups &groups,
                           hipStream_t stream) {
-  SplitKVArgs a = a_in;
-  const int rows = splitkv_rows(a.n_streams, a.n_pos, groups.gsize);
   dim3 grid(a.n_chunks, groups.n_groups, a.B);
   if (a.block_table)
     hipLaunchKernelGGL(splitkv_kernel<true>, grid, dim3(kThreads), 0, stream,
@@ -530,14 +610,6 @@ hipError_t launch_splitkv(const SplitKVArgs &a_in, const HeadGroups &groups,
   else
     hipLaunchKernelGGL(splitkv_kernel<false>, grid, dim3(kThreads), 0, stream,
                        a, groups);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.n_chunks > 32)
-    hipLaunchKernelGGL(splitkv_merge_kernel<64>, dim3(rows, groups.n_groups, a.B),
-                       dim3(256), 0, stream, a, groups);
-  else
-    hipLaunchKernelGGL(splitkv_merge_kernel<16>, dim3(rows, groups.n_groups, a.B),
-                       dim3(256), 0, stream, a, groups);
   return hipGetLastError();
 }
 

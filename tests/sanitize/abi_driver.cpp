@@ -28,9 +28,13 @@ static void sizing(int op, int B, int Hq, int Hkv, int T_out, int64_t len,
   const size_t need = orthros_workspace_bytes(op, B, Hq, Hkv, 128, T_out, len,
                                               map);
   CHECK(need > 0, "op %d B=%d Hq=%d Hkv=%d: no workspace size", op, B, Hq, Hkv);
+  const size_t cb = orthros_workspace_counter_bytes(op, B, Hq, Hkv, 128, T_out,
+                                                    len, map);
+  CHECK(cb >= (size_t)B * 8 && cb % 256 == 0 && cb < need,
+        "op %d B=%d: counter bytes %zu of %zu", op, B, cb, need);
   for (int exact = 0; exact < 2; ++exact) {
     const size_t nb = exact ? need : need - 1;
-    void *ws = malloc(nb);
+    void *ws = calloc(nb, 1);  // zero counters, as the calls require
     const int before = stub_splitkv_launches;
     int rc;
     if (op == ORTHROS_OP_GLOBAL_XATTN)
@@ -124,6 +128,18 @@ int main() {
                               128, 300, 100, NULL, ORTHROS_BF16, NULL) == 0,
           "valid window call");
     CHECK(stub_launches == n0 + 1, "window launches");
+  }
+  // the no-allocation decode pair near its limit: the partials follow the
+  // fixed counter region inside the static array (here the stand-in's host
+  // array, every byte of the partials written)
+  {
+    const int n0 = stub_splitkv_launches;
+    CHECK(orthros_decode_pair_noalloc(F, F, (float *)F, (float *)F, (float *)F,
+                                      (float *)F, F, F, F, F, (int32_t *)F, F,
+                                      F, 64, 32, 8, 128, 60007, 60000, 16, NULL,
+                                      ORTHROS_BF16, NULL) == ORTHROS_OK,
+          "no-allocation decode pair");
+    CHECK(stub_splitkv_launches == n0 + 1, "no-allocation launch");
   }
   if (failures) {
     fprintf(stderr, "%d failures\n", failures);

@@ -6,12 +6,13 @@
 //
 // Every launcher counts its calls (a rejected call must launch nothing).
 // The split-KV launcher also writes every byte of the workspace regions the
-// kernels use (lengths, partial maxima and sums, partial outputs), computed
+// kernels use (counters, partial maxima and sums, partial outputs), computed
 // from the arguments it receives: with a workspace allocated at exactly the
 // size orthros_workspace_bytes returned, any region past its end is a heap
 // overflow that the sanitizer reports.
 #include <string.h>
 
+#include "../../include/orthros.h"
 #include "../../long_context_prefill_swa_amd/csrc/common.h"
 
 extern "C" int stub_launches = 0;
@@ -103,10 +104,23 @@ hipError_t launch_splitkv(const SplitKVArgs &a, const HeadGroups &groups,
   const int rows = splitkv_rows(a.n_streams, a.n_pos, groups.gsize);
   const int64_t parts = (int64_t)a.B * groups.n_groups * a.n_chunks * rows;
   if (a.ws_acc_offset < 2 * parts) return hipErrorInvalidValue;  // overlap
-  if ((char *)a.ws < (char *)(a.ws_len + a.B)) return hipErrorInvalidValue;
-  memset(a.ws_len, 0x5a, sizeof(int32_t) * (size_t)a.B);
+  const int64_t n_counters = (int64_t)a.B * (groups.n_groups + 1);
+  if ((char *)a.ws < (char *)(a.counters + n_counters))
+    return hipErrorInvalidValue;
+  // the kernel's counters are read-modify-write and left as they were
+  for (int64_t i = 0; i < n_counters; ++i) a.counters[i] += 0;
   memset(a.ws, 0x5a, sizeof(float) * 2 * (size_t)parts);
   memset(a.ws + a.ws_acc_offset, 0x5a, sizeof(float) * 128 * (size_t)parts);
+  return hipSuccess;
+}
+
+// The no-allocation scratch array: a host array of the same size, zero at
+// load like the device one.
+static unsigned char host_scratch[ORTHROS_NOALLOC_SCRATCH_BYTES]
+    __attribute__((aligned(256)));
+
+hipError_t noalloc_scratch_ptr(void **out) {
+  *out = host_scratch;
   return hipSuccess;
 }
 

@@ -52,7 +52,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_strerror(L):
-    assert L.orthros_abi_version() == 6
+    assert L.orthros_abi_version() == 7
     for code in (OK, EINVAL, EUNSUP, ECAP, EWS, EHIP):
         assert L.orthros_strerror(code)
     assert b"unknown" in L.orthros_strerror(42)
@@ -171,6 +171,27 @@ def test_workspace_bytes(L):
     assert ws(1, 1, 2, 2, 16, 1, 64) == 0
     # no map and Hq not a multiple of Hkv: invalid
     assert ws(1, 1, 5, 2, 128, 1, 100) == 0
+
+
+def test_workspace_counter_bytes(L):
+    """The arrival counters: one int32 per (batch entry, head group) and one
+    per batch entry, padded to 256 bytes, at the front of the workspace;
+    they depend on B and the head grouping, not on the lengths."""
+    def cb(*a, m=None):
+        return L.orthros_workspace_counter_bytes(*a, m)
+    # 32 query heads on 8 KV heads: a decode pair has 2 rows per query head,
+    # so each KV head's 4 heads form one group (8 rows): 8 groups
+    assert cb(2, 64, 32, 8, 128, 1, 33024) == 64 * 9 * 4
+    assert cb(2, 64, 32, 8, 128, 1, 66048) == 64 * 9 * 4
+    assert cb(2, 1, 32, 8, 128, 1, 131072) == 256
+    # one output row of 32 heads: 8 groups of 4 rows
+    assert cb(1, 1, 32, 8, 128, 1, 131072) == 256
+    assert cb(1, 100, 32, 8, 128, 1, 4096) == (100 * 9 * 4 + 255) // 256 * 256
+    for a in ((9, 1, 4, 2, 128, 1, 100), (2, 0, 4, 2, 128, 1, 100),
+              (1, 4, 32, 8, 128, 2048, 8192), (1, 1, 5, 2, 128, 1, 100)):
+        assert cb(*a) == 0 and L.orthros_workspace_bytes(*a, None) == 0
+    for a in ((2, 64, 32, 8, 128, 1, 33024), (1, 1, 32, 8, 128, 1, 131072)):
+        assert 0 < cb(*a) < L.orthros_workspace_bytes(*a, None)
 
 
 def imap(m):
@@ -425,6 +446,15 @@ def test_noalloc_decode_pair_rejects_sizes_beyond_its_scratch(L):
                                        BF16, None)
     assert rc == EWS
     assert "no-allocation" in last(L)
+    # counters beyond their fixed region: 2048 entries x (8 groups + 1)
+    # int32 = 72 KiB, while the partials alone would fit
+    assert L.orthros_workspace_counter_bytes(2, 2048, 8, 8, 128, 1, 100,
+                                             None) > 64 << 10
+    assert L.orthros_workspace_bytes(2, 2048, 8, 8, 128, 1, 100, None) < limit
+    rc = L.orthros_decode_pair_noalloc(*[FAKE] * 10, FAKE, FAKE, FAKE, 2048, 8,
+                                       8, 128, 101, 100, 16, None, BF16, None)
+    assert rc == EWS
+    assert "counters" in last(L)
     # ordinary argument errors come first, as in orthros_decode_pair
     assert L.orthros_decode_pair_noalloc(*[FAKE] * 10, FAKE, FAKE, FAKE, 2, 4,
                                          2, 128, 100, 101, 16, None, BF16,
