@@ -443,11 +443,12 @@ size_t orthros_workspace_bytes(int op, int B, int Hq, int Hkv, int D,
 
 /*
  * Leading bytes of that workspace holding the arrival counters, which must
- * be zero when a call starts (every call leaves them zero). The split-KV
- * calls run as one launch: each workgroup writes its partial result, then
- * counts itself in, and the last to arrive for a (batch entry, head group)
- * combines the partials (in a decode step the last to leave a batch entry
- * also advances its length). Depends on B and the head grouping only.
+ * be zero when a call starts (every call leaves them zero). A split-KV call
+ * whose grid the chip holds at once runs as one launch: each workgroup
+ * writes its partial result, then counts itself in, and the last to arrive
+ * for a (batch entry, head group) combines the partials (in a decode step
+ * the last to leave a batch entry also advances its length); larger grids
+ * merge in a second launch. Depends on B and the head grouping only.
  * Arguments and zero returns as orthros_workspace_bytes; pure host function.
  */
 size_t orthros_workspace_counter_bytes(int op, int B, int Hq, int Hkv, int D,

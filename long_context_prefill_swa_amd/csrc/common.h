@@ -183,9 +183,12 @@ struct SplitKVArgs {
   int n_chunks;
   float *ws;                 // partials: (max, sum) pairs, then outputs
   int64_t ws_acc_offset;     // float offset of the unnormalised outputs
-  int32_t *counters;         // [B * n_groups] arrivals per (batch, group),
-                             // then [B] (decode) per batch entry; zero at
-                             // the start of a call, left zero at its end
+  int fused;                 // 1: merge in the same launch; 0: merge kernel
+  int32_t *counters;         // one launch: [B * n_groups] arrivals per
+                             // (batch, group), then [B] (decode) per batch
+                             // entry; zero at the start of a call, left zero
+  int32_t *ws_len;           // two launches, decode: per-batch old length
+                             // or -1 (skipped), for the merge kernel
   int *flag;
   // Paged cache (block_table != nullptr): k_cache / v_cache are pools of
   // n_pages pages [n_pages, n_kv_heads, page_size, D]; key i of batch entry
@@ -198,6 +201,8 @@ struct SplitKVArgs {
 };
 int splitkv_rows(int n_streams, int n_pos, int gsize);
 size_t splitkv_counter_bytes(int B, int n_groups);
+size_t splitkv_len_bytes(int B);
+bool splitkv_fused(int B, int n_groups, int n_chunks);
 // Device address, on the current device, of the no-allocation decode pair's
 // static scratch array (looked up on the first call on that device).
 hipError_t noalloc_scratch_ptr(void **out);

@@ -138,15 +138,14 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 struct SplitPlan {
   bool use = false;
   int rows = 0, chunk = 0, n_chunks = 0;
+  bool fused = false;
   size_t ws_bytes = 0;
 };
 
-// Chunks of at most 4096 keys on a contiguous cache, 2048 on a paged one (a
-// chunk spans at most 64 pages). A decode step's workspace is sized for the
-// paged plan, which never needs less than the contiguous one: the chunk the
-// contiguous plan picks is at least as large, so it has no more chunks.
-constexpr int kChunkContiguous = 4096;
-constexpr int kChunkPaged = 2048;
+// Chunks of at most 4096 keys for output rows, 2048 for a decode step (its
+// cache may be paged, and a chunk spans at most 64 pages).
+constexpr int kChunkRows = 4096;
+constexpr int kChunkDecode = 2048;
 
 SplitPlan plan_split(int B, int n_streams, int n_pos, const HeadGroups &g,
                      int D, int64_t max_len, int max_chunk) {
@@ -158,6 +157,7 @@ SplitPlan plan_split(int B, int n_streams, int n_pos, const HeadGroups &g,
   p.use = true;
   p.chunk = splitkv_pick_chunk(B, g.n_groups, max_len, max_chunk);
   p.n_chunks = (int)((max_len + p.chunk - 1) / p.chunk);
+  p.fused = splitkv_fused(B, g.n_groups, p.n_chunks);
   p.ws_bytes = splitkv_ws_bytes(B, g.n_groups, p.rows, p.n_chunks, D);
   return p;
 }
@@ -166,8 +166,10 @@ SplitPlan plan_split(int B, int n_streams, int n_pos, const HeadGroups &g,
 // splitkv_counter_bytes), the partials the rest.
 void fill_ws(SplitKVArgs *a, void *ws, const SplitPlan &p, int B,
              int n_groups, size_t counter_region) {
+  a->fused = p.fused ? 1 : 0;
   a->counters = (int32_t *)ws;
-  a->ws = (float *)((char *)ws + counter_region);
+  a->ws_len = (int32_t *)((char *)ws + counter_region);
+  a->ws = (float *)((char *)ws + counter_region + splitkv_len_bytes(B));
   const int64_t parts = (int64_t)B * n_groups * p.n_chunks * p.rows;
   a->ws_acc_offset = (parts * 2 + 63) / 64 * 64;
   a->chunk = p.chunk;
@@ -193,9 +195,9 @@ bool query_plan(int op, int B, int Hq, int Hkv, int D, int T_out,
   memcpy(g_msg, saved, sizeof(g_msg));
   if (rc != ORTHROS_OK) return false;
   if (op == ORTHROS_OP_GLOBAL_XATTN)
-    *p = plan_split(B, 1, T_out, *g, D, max_len, kChunkContiguous);
+    *p = plan_split(B, 1, T_out, *g, D, max_len, kChunkRows);
   else if (op == ORTHROS_OP_DECODE_PAIR)
-    *p = plan_split(B, 2, 1, *g, D, max_len, kChunkPaged);
+    *p = plan_split(B, 2, 1, *g, D, max_len, kChunkDecode);
   else
     return false;
   return p->use;
@@ -354,8 +356,7 @@ int orthros_global_xattn(const void *qx_pre, const float *alpha_x,
   hipError_t e;
   const bool mfma =
       mfma_eligible(dtype, D, T, {qx_pre, alpha_x, beta_x, k_cache, v_cache, o_x});
-  const SplitPlan plan =
-      plan_split(B, 1, T_out, groups, D, T, kChunkContiguous);
+  const SplitPlan plan = plan_split(B, 1, T_out, groups, D, T, kChunkRows);
   if (mfma && plan.use) {
     if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))
       return fail(ORTHROS_EWORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, got %zu",
@@ -446,12 +447,9 @@ int decode_pair_impl(const void *q_pre, const void *qx_pre,
   const bool mfma = mfma_eligible(
       dtype, D, max_len_after, {q_pre, qx_pre, alpha, beta, alpha_x, beta_x, k_new, v_new,
                  k_cache, v_cache, o, o_x});
-  // checked against the workspace query's (paged) size, launched with the
-  // contiguous plan, which fits in it
-  const size_t ws_need =
-      plan_split(B, 2, 1, groups, D, max_len_after, kChunkPaged).ws_bytes;
   const SplitPlan plan =
-      plan_split(B, 2, 1, groups, D, max_len_after, kChunkContiguous);
+      plan_split(B, 2, 1, groups, D, max_len_after, kChunkDecode);
+  const size_t ws_need = plan.ws_bytes;
   hipError_t e;
   size_t counter_region = splitkv_counter_bytes(B, groups.n_groups);
   if (mfma && plan.use && from_scratch) {
@@ -657,7 +655,7 @@ int orthros_decode_pair_paged(const void *q_pre, const void *qx_pre,
                       v_new, k_pool, v_pool, o, o_x}))
     return fail(ORTHROS_EINVAL, "tensors must be 16-byte aligned");
   const SplitPlan plan =
-      plan_split(B, 2, 1, groups, D, max_len_after, kChunkPaged);
+      plan_split(B, 2, 1, groups, D, max_len_after, kChunkDecode);
   if (!plan.use)
     return fail(ORTHROS_EUNSUPPORTED, "no split plan for these sizes");
   if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws))

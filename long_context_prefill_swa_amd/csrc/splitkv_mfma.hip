@@ -31,12 +31,23 @@
 // masked, so the loop has no data-dependent branch.
 //
 // After the loop the 4 waves merge in LDS and the workgroup writes one
-// (max, sum, unnormalised output) partial per row. It then counts itself in
-// at its (batch, head group): the last workgroup to arrive combines the
-// partials of all chunks with log-sum-exp weights, normalises and writes the
-// output rows. In a decode step the last group of a batch entry to finish
-// its merge then advances the cache length. One launch per call; the
-// arrival counters sit in the workspace, start at zero and are left at zero.
+// (max, sum, unnormalised output) partial per row. The partials of all
+// chunks are then combined with log-sum-exp weights, normalised and written
+// as the output rows, in one of two ways:
+//  * one launch (a grid that the chip holds at once, such as a long
+//    prompt's output row): each workgroup counts itself in at its (batch,
+//    head group) and the last to arrive combines the group's partials; in
+//    a decode step the last workgroup of a batch entry to finish advances
+//    its cache length. The arrival counters sit in the workspace, start at
+//    zero and are left at zero.
+//  * two launches (a grid of many rounds, such as a decode step over many
+//    sequences): splitkv_merge_kernel combines after the split kernel, one
+//    workgroup per (row, head group, batch), and advances the lengths from
+//    the old ones the split kernel left in the workspace. Here the split
+//    workgroups end as soon as their partials are issued; waiting for the
+//    stores and counting in would hold each of the many workgroups' slots
+//    a few microseconds longer (a B = 64 decode step measured 2-6% slower
+//    in one launch).
 #include "common.h"
 
 namespace orthros {
@@ -263,7 +274,10 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
       // skipped (the length is left unchanged): chunk 0 of each group
       // writes the group's output rows as zeros
       if (c == 0) {
-        if (gi == 0 && tid == 0) atomicOr(a.flag, 1);
+        if (gi == 0 && tid == 0) {
+          atomicOr(a.flag, 1);
+          if (!a.fused) a.ws_len[b] = -1;
+        }
         const int r = tid >> 4, d0 = (tid & 15) * 8;
         if (r < rows) {
           const int hq = groups.q[gi][r % gsize];
@@ -291,11 +305,14 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
       }
     }
   };
+  // two launches: the merge kernel reads the old length from the workspace
+  if (!a.fused && a.cache_len && c == 0 && gi == 0 && tid == 0)
+    a.ws_len[b] = (int32_t)n_old;
   const int64_t pos_base = a.cache_len ? n_old : a.pos0;  // row 0's position
   const int64_t hi_max = pos_base + a.n_pos - 1;
   const int64_t k_begin = (int64_t)c * a.chunk;
   if (k_begin > hi_max) {
-    leave();
+    if (a.fused) leave();
     return;
   }
   // keys of this workgroup: [k_begin, k_stop)
@@ -569,15 +586,23 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
         }
       }
       const int pi = c * rows + r;
-      if (f == 0)
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(u32x2, f32x2{M, L}), pv.ml, pi * 8, 0,
-            kDeviceScope);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o),
-                                             pv.acc, pi * (D * 4) + f * 16, 0,
-                                             kDeviceScope);
+      const u32x2 mlw = __builtin_bit_cast(u32x2, f32x2{M, L});
+      const u32x4 ow = __builtin_bit_cast(u32x4, o);
+      if (a.fused) {  // read back within this launch, by another XCD
+        if (f == 0)
+          __builtin_amdgcn_raw_buffer_store_b64(mlw, pv.ml, pi * 8, 0,
+                                                kDeviceScope);
+        __builtin_amdgcn_raw_buffer_store_b128(ow, pv.acc, pi * (D * 4) + f * 16,
+                                               0, kDeviceScope);
+      } else {  // read by the merge kernel, after the kernel boundary
+        if (f == 0)
+          __builtin_amdgcn_raw_buffer_store_b64(mlw, pv.ml, pi * 8, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(ow, pv.acc, pi * (D * 4) + f * 16,
+                                               0, 0);
+      }
     }
   }
+  if (!a.fused) return;
 
   // ---- arrival; the last workgroup of (batch, group) merges ---------------
   // Chunks with work for this batch entry: those starting at or before its
@@ -599,6 +624,112 @@ __global__ __launch_bounds__(kThreads, 2) void splitkv_kernel(
   leave();
 }
 
+// Two-launch mode: one workgroup per (row, head group, batch), LANES chunk
+// lanes of 256 / LANES threads. Thread (q, part): chunks c_lo + q,
+// c_lo + q + LANES, ... and channels CH part .. CH part + CH - 1 (CH = D
+// LANES / 256). Every load of a chunk is issued before its maximum is
+// tested, so a row over up to LANES chunks costs one memory round trip; the
+// lanes are then combined in LDS. 64 lanes serve rows over more than 32
+// chunks; 16 lanes, with a quarter of the LDS and so more resident
+// workgroups, serve a decode step's rows over a few.
+template <int LANES>
+__global__ __launch_bounds__(256) void splitkv_merge_kernel(SplitKVArgs a,
+                                                            HeadGroups groups) {
+  constexpr int kParts = 256 / LANES, CH = D / kParts;
+  __shared__ float sm_m[LANES], sm_l[LANES], sm_f[LANES];
+  __shared__ float sm_sum;
+  __shared__ float sm_acc[LANES][D + 4];
+  const int r = blockIdx.x, gi = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int gsize = groups.gsize;
+  const int rows = a.n_streams * a.n_pos * gsize;
+  const int s = r / (a.n_pos * gsize);
+  const int j = (r / gsize) % a.n_pos;
+  const int h = groups.q[gi][r % gsize];
+  int64_t n_old = 0;
+  if (a.cache_len) {
+    n_old = a.ws_len[b];
+    // a skipped entry: the split kernel wrote its zero rows
+    if (n_old < 0) return;
+  }
+  // Decode: the cache now holds n_old + 1 rows for this batch entry. Every
+  // split workgroup has finished reading (kernel boundary), and the merge
+  // reads the old length from the workspace, so this write races with none.
+  // Row 0 of group 0 always exists (its first query head).
+  if (a.cache_len && r == 0 && gi == 0 && tid == 0)
+    ((int32_t *)a.cache_len)[b] = (int32_t)(n_old + 1);
+  if (h < 0) return;
+
+  const int q = tid / kParts, part = tid % kParts, d0 = CH * part;
+  float M = -INFINITY, L = 0.0f;
+  f32x4 o[CH / 4];
+#pragma unroll
+  for (int k = 0; k < CH / 4; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t t = (a.cache_len ? n_old : a.pos0) + j;
+  const int Ws = a.W[s];
+  const int64_t lo = (Ws > 0 && t - Ws + 1 > 0) ? t - Ws + 1 : 0;
+  const int c_lo = (int)(lo / a.chunk), c_hi = (int)(t / a.chunk);
+  for (int cc = c_lo + q; cc <= c_hi; cc += LANES) {
+    const int64_t pi = ws_part_index(a, groups.n_groups, rows, b, gi, cc, r);
+    const float mc = a.ws[pi * 2];
+    const float lc = a.ws[pi * 2 + 1];
+    const f32x4 *pacc =
+        (const f32x4 *)(a.ws + (int64_t)a.ws_acc_offset + pi * D + d0);
+    f32x4 u[CH / 4];
+#pragma unroll
+    for (int k = 0; k < CH / 4; ++k) u[k] = pacc[k];
+    if (mc != -INFINITY) {  // a chunk with keys in this row's range
+      const float Mn = fmaxf(M, mc);
+      const float fo = exp2f(M - Mn), fn = exp2f(mc - Mn);
+      L = L * fo + lc * fn;
+#pragma unroll
+      for (int k = 0; k < CH / 4; ++k) o[k] = o[k] * fo + u[k] * fn;
+      M = Mn;
+    }
+  }
+  if (part == 0) {
+    sm_m[q] = M;
+    sm_l[q] = L;
+  }
+#pragma unroll
+  for (int k = 0; k < CH / 4; ++k) *(f32x4 *)&sm_acc[q][d0 + 4 * k] = o[k];
+  __syncthreads();
+  if (tid < LANES) {
+    // the first LANES threads: the row maximum over the lanes, each lane's
+    // weight, and the sum (xor shuffles within the LANES-wide group)
+    const float mq = sm_m[tid];
+    float Mx = mq;
+#pragma unroll
+    for (int sh = LANES / 2; sh >= 1; sh >>= 1)
+      Mx = fmaxf(Mx, __shfl_xor(Mx, sh, 64));
+    const float f = (mq == -INFINITY) ? 0.0f : exp2f(mq - Mx);
+    sm_f[tid] = f;
+    float lsum = f * sm_l[tid];
+#pragma unroll
+    for (int sh = LANES / 2; sh >= 1; sh >>= 1) lsum += __shfl_xor(lsum, sh, 64);
+    if (tid == 0) sm_sum = lsum;
+  }
+  __syncthreads();
+  if (tid < D / 2) {
+    // thread tid: channels 2 tid, 2 tid + 1
+    float out0 = 0.0f, out1 = 0.0f;
+#pragma unroll 8
+    for (int qq = 0; qq < LANES; ++qq) {
+      const float f = sm_f[qq];
+      const float2 v = *(const float2 *)&sm_acc[qq][2 * tid];
+      out0 += f * v.x;
+      out1 += f * v.y;
+    }
+    const float Lx = sm_sum;
+    const float inv = Lx > 0.0f ? 1.0f / Lx : 0.0f;
+    const uint32_t lo16 = __builtin_bit_cast(uint16_t, (__bf16)(out0 * inv));
+    const uint32_t hi16 = __builtin_bit_cast(uint16_t, (__bf16)(out1 * inv));
+    uint16_t *dst = (uint16_t *)a.o[s] +
+                    (((int64_t)b * a.n_pos + j) * a.Hq + h) * D + 2 * tid;
+    *(uint32_t *)dst = lo16 | (hi16 << 16);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_splitkv(const SplitKVArgs &a, const HeadGroups &groups,
@@ -609,6 +740,15 @@ hipError_t launch_splitkv(const SplitKVArgs &a, const HeadGroups &groups,
                        a, groups);
   else
     hipLaunchKernelGGL(splitkv_kernel<false>, grid, dim3(kThreads), 0, stream,
+                       a, groups);
+  if (a.fused) return hipGetLastError();
+  const int rows = a.n_streams * a.n_pos * groups.gsize;
+  const dim3 mgrid(rows, groups.n_groups, a.B);
+  if (a.n_chunks > 32)
+    hipLaunchKernelGGL(splitkv_merge_kernel<64>, mgrid, dim3(256), 0, stream,
+                       a, groups);
+  else
+    hipLaunchKernelGGL(splitkv_merge_kernel<16>, mgrid, dim3(256), 0, stream,
                        a, groups);
   return hipGetLastError();
 }

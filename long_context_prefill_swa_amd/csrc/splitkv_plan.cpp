@@ -33,18 +33,28 @@ int splitkv_pick_chunk(int B, int n_groups, int64_t max_len, int max_chunk) {
 
 // Workspace layout: the arrival counters (int32, one per (batch, head group)
 // and one per batch entry, padded to 256 bytes; they depend on B and the
-// head grouping only), then (max, sum) float pairs of every partial, padded
-// to 64 floats, then the unnormalised output rows. Must agree with the
-// offsets set by the caller.
+// head grouping only), the old lengths of a two-launch decode step (int32
+// per batch entry, padded to 256 bytes), then (max, sum) float pairs of
+// every partial, padded to 64 floats, then the unnormalised output rows.
+// Must agree with the offsets set by the caller.
 size_t splitkv_counter_bytes(int B, int n_groups) {
   return ((size_t)B * (n_groups + 1) * 4 + 255) / 256 * 256;
 }
 
+size_t splitkv_len_bytes(int B) { return ((size_t)B * 4 + 255) / 256 * 256; }
+
 size_t splitkv_ws_bytes(int B, int n_groups, int rows, int n_chunks, int Dh) {
   const size_t parts = (size_t)B * n_groups * n_chunks * rows;
   const size_t ml_floats = (parts * 2 + 63) / 64 * 64;
-  return splitkv_counter_bytes(B, n_groups) +
+  return splitkv_counter_bytes(B, n_groups) + splitkv_len_bytes(B) +
          (ml_floats + parts * (size_t)Dh) * 4;
+}
+
+// One launch when the chip holds the whole grid at once (two workgroups
+// per compute unit, 256 compute units): the last workgroup of each group
+// then merges while no other work waits for its slot.
+bool splitkv_fused(int B, int n_groups, int n_chunks) {
+  return (int64_t)B * n_groups * n_chunks <= 512;
 }
 
 }  // namespace orthros

@@ -105,10 +105,12 @@ hipError_t launch_splitkv(const SplitKVArgs &a, const HeadGroups &groups,
   const int64_t parts = (int64_t)a.B * groups.n_groups * a.n_chunks * rows;
   if (a.ws_acc_offset < 2 * parts) return hipErrorInvalidValue;  // overlap
   const int64_t n_counters = (int64_t)a.B * (groups.n_groups + 1);
-  if ((char *)a.ws < (char *)(a.counters + n_counters))
+  if ((char *)a.ws_len < (char *)(a.counters + n_counters) ||
+      (char *)a.ws < (char *)(a.ws_len + a.B))
     return hipErrorInvalidValue;
   // the kernel's counters are read-modify-write and left as they were
   for (int64_t i = 0; i < n_counters; ++i) a.counters[i] += 0;
+  memset(a.ws_len, 0x5a, sizeof(int32_t) * (size_t)a.B);
   memset(a.ws, 0x5a, sizeof(float) * 2 * (size_t)parts);
   memset(a.ws + a.ws_acc_offset, 0x5a, sizeof(float) * 128 * (size_t)parts);
   return hipSuccess;
