@@ -503,10 +503,23 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
   }
 
   struct Item { int hi, s, qb; };
-  auto decode = [&](int it) {
-    const int hi = it / per_head, rr = it % per_head;
-    const int s = rr >= n_base;
-    return Item{hi, s, s ? out_lo + (rr - n_base) : base_lo + rr};
+  // Work-list cursor (item index, head slot, index within the head's
+  // items), advanced one item at a time and held at the last item, so that
+  // no item number is ever divided.
+  struct Cur { int it, hi, rr; };
+  auto adv = [&](Cur c) {
+    if (c.it + 1 < n_it) {
+      ++c.it;
+      if (++c.rr == per_head) {
+        c.rr = 0;
+        ++c.hi;
+      }
+    }
+    return c;
+  };
+  auto decode = [&](Cur c) {
+    const int s = c.rr >= n_base;
+    return Item{c.hi, s, s ? out_lo + (c.rr - n_base) : base_lo + c.rr};
   };
 
   // staging: thread -> rows tid/16 + 32 u (u = 0, 1), one 16-byte chunk;
@@ -516,8 +529,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     uint4 q0, q1, g0, g1;
     float lse, delta;
   };
-  auto load = [&](Stage &st, int it) {
-    const Item itm = decode(it);
+  auto load = [&](Stage &st, Cur cu) {
+    const Item itm = decode(cu);
     const int h = slot_head(gh, itm.hi);
     const int nrows = itm.s ? a.T_out : a.T;
     const uint16_t *qsrc = itm.s ? a.qx : a.q;
@@ -549,8 +562,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     }
     return make_uint4(o4[0], o4[1], o4[2], o4[3]);
   };
-  auto store = [&](const Stage &st, int it) {
-    const Item itm = decode(it);
+  auto store = [&](const Stage &st, Cur cu) {
+    const Item itm = decode(cu);
     const float *al = sm.ab[itm.hi][2 * itm.s];
     const float *be = sm.ab[itm.hi][2 * itm.s + 1];
     *(uint4 *)&sm.q[srow][sd0] = qrow(st.q0, al, be);
@@ -562,8 +575,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
       sm.delta[tid] = st.delta;
     }
   };
-  auto block = [&](int it) {
-    const Item itm = decode(it);
+  auto block = [&](Cur cu) {
+    const Item itm = decode(cu);
     const int nrows = itm.s ? a.T_out : a.T;
     const int pos0 = (itm.s ? T_in : 0) + itm.qb * 64;  // position of row 0
     const int Ws = itm.s ? a.T : a.W;
@@ -610,6 +623,19 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
         if (!none[1]) quarter(1);
       }
       bf16x8 pop, dsop;
+      if (all_in[0] & all_in[1]) {  // no masking in this half
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float lv[4] = {lse4[h2].x, lse4[h2].y, lse4[h2].z, lse4[h2].w};
+          const float dv4[4] = {del4[h2].x, del4[h2].y, del4[h2].z, del4[h2].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pr = __builtin_amdgcn_exp2f(sc[h2][i] - lv[i]);
+            pop[4 * h2 + i] = (__bf16)pr;
+            dsop[4 * h2 + i] = (__bf16)(pr * (dp[h2][i] - dv4[i]));
+          }
+        }
+      } else
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const int rq0 = 32 * half + 16 * h2;
@@ -620,10 +646,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
         for (int i = 0; i < 4; ++i) {
           const int rl = rq0 + 4 * g4 + i;
           const int p = pos0 + rl;
-          const bool ok = !none[h2] &&
-                          (all_in[h2] || (itm.qb * 64 + rl < nrows && key < a.T &&
-                                          key <= p && key >= range_lo(p, Ws)));
-          const float pr = ok ? __builtin_amdgcn_exp2f(sc[h2][i] - lv[i]) : 0.0f;
+          // branch-free: exp2(-inf) = 0 outside the ranges
+          const bool in = (itm.qb * 64 + rl < nrows) & (key < a.T) &
+                          (key <= p) & (key >= range_lo(p, Ws));
+          const bool ok = !none[h2] & (all_in[h2] | in);
+          const float pr =
+              __builtin_amdgcn_exp2f(ok ? sc[h2][i] - lv[i] : -INFINITY);
           pop[4 * h2 + i] = (__bf16)pr;
           dsop[4 * h2 + i] = (__bf16)(pr * (dp[h2][i] - dv4[i]));
         }
@@ -647,26 +675,32 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
   // past the last block re-read it (unused), so that every block issues the
   // same loads; a counted loop of block pairs keeps one path through it.
   Stage sA = {}, sB = {};
-  load(sA, 0);
-  load(sB, min(1, n_it - 1));
-  int it = 0;
-  for (; it + 1 < n_it; it += 2) {
+  Cur c0 = {0, 0, 0};     // the block to compute
+  Cur c2 = adv(c0);       // two cursors ahead: the next loads
+  load(sA, c0);
+  load(sB, c2);
+  c2 = adv(c2);
+  for (; c0.it + 1 < n_it;) {
     __syncthreads();  // readers of the previous block are done (and ab)
-    store(sA, it);
+    store(sA, c0);
     __syncthreads();
-    load(sA, min(it + 2, n_it - 1));
-    block(it);
+    load(sA, c2);
+    c2 = adv(c2);
+    block(c0);
+    c0 = adv(c0);
     __syncthreads();
-    store(sB, it + 1);
+    store(sB, c0);
     __syncthreads();
-    load(sB, min(it + 3, n_it - 1));
-    block(it + 1);
+    load(sB, c2);
+    c2 = adv(c2);
+    block(c0);
+    c0 = adv(c0);
   }
-  if (it < n_it) {
+  if ((n_it & 1) == 1) {
     __syncthreads();
-    store(sA, it);
+    store(sA, c0);
     __syncthreads();
-    block(it);
+    block(c0);
   }
 
   // dK = dS^T (c q) / (c sqrt(D)) with c sqrt(D) = log2(e); dV = P^T dO
