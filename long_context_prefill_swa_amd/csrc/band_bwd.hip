@@ -18,14 +18,15 @@
 //    Pass 1 over the band's 64-key tiles forms S^T = K Q^T and the row's
 //    log-sum-exp; pass 2 forms S^T and dP^T = V dO^T again, dS^T, and
 //    dQ^T += K^T dS^T (K^T read with ds_read_b64_tr_b16). It writes
-//    dq_pre, the row's log-sum-exp and dO . o, and per 32-row block the
-//    channel sums that make d alpha and d beta.
+//    dq_pre, the row's log-sum-exp and dO . o, per 32-row block the
+//    channel sums that make d alpha and d beta, and the query operand it
+//    formed (bf16 of the scaled alpha q + beta) for the dK/dV kernel.
 //  * bwd_dkv_kernel (both streams): 8 waves, each 16 keys of one KV head,
 //    over every query head of that KV head and every 64-row block of either
 //    stream that sees the keys (16-row quarters outside a wave's band are
 //    skipped): S = Q K^T and dP = dO V^T with K, V held in
 //    registers, then dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T read
-//    transposed from LDS.
+//    transposed from LDS. Q comes ready-made from the dQ kernels.
 //  * bwd_reduce_kernel: the per-block channel sums, added in a fixed order.
 // All softmax arithmetic is fp32 in base 2 (log2(e)/sqrt(D) folded into the
 // query operand, as in the forward kernels); P and dS enter the MFMA as bf16.
@@ -221,6 +222,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
         const float qv = (e & 1) ? bf16_hi(qw[e >> 1]) : bf16_lo(qw[e >> 1]);
         qop[h2][c4][e] = (__bf16)(sm.ab[hs][0][d0 + e] * qv + sm.ab[hs][1][d0 + e]);
       }
+      // the dK/dV kernel reads these operands rather than forming them again
+      if (row_ok[h2])
+        *(uint4 *)(a.qa + off + d0) = __builtin_bit_cast(uint4, qop[h2][c4]);
     }
   }
 
@@ -256,7 +260,6 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
     for (int dt = 0; dt < 8; ++dt) acc[h2][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int j16 = col;
 
-  const int n_tiles = kt_hi - kt_lo + 1;
   auto next_tile = [&](int kt) {
     __syncthreads();  // the previous tile's readers are done
     store();
@@ -439,7 +442,6 @@ struct DkvSmem {
   uint16_t q[64][kS];
   uint16_t g[64][kS];
   float lse[64], delta[64];
-  float ab[GS][4][D];  // alpha, beta, alpha', beta' of the group's heads
 };
 
 constexpr int kKvWaves = 8;                 // 16 keys each
@@ -462,7 +464,6 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
   const int k0 = kt * kKvKeys;
   const int kw = k0 + 16 * w;          // first key of this wave
   const int key = kw + col;            // this lane's key (B columns)
-  const float qs = kLog2e * rsqrtf((float)D);
 
   // K and V rows of this wave's keys as B operands (channels 32 c4 + 8 g4)
   bf16x8 kop[4], vop[4];
@@ -495,13 +496,6 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
   while (n_heads < GS && slot_head(gh, n_heads) >= 0) ++n_heads;
   const int n_it = n_heads * per_head;
 
-  for (int i = tid; i < n_heads * 4 * D; i += kKvThreads) {
-    const int hi = i / (4 * D), which = (i / D) % 4, d = i % D;
-    const float *src = which == 0 ? a.alpha : which == 1 ? a.beta
-                     : which == 2 ? a.alpha_x : a.beta_x;
-    sm.ab[hi][which][d] = src[slot_head(gh, hi) * D + d] * qs;
-  }
-
   struct Item { int hi, s, qb; };
   // Work-list cursor (item index, head slot, index within the head's
   // items), advanced one item at a time and held at the last item, so that
@@ -533,7 +527,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     const Item itm = decode(cu);
     const int h = slot_head(gh, itm.hi);
     const int nrows = itm.s ? a.T_out : a.T;
-    const uint16_t *qsrc = itm.s ? a.qx : a.q;
+    const uint16_t *qsrc = itm.s ? a.qax : a.qa;
     const uint16_t *gsrc = itm.s ? a.d_ox : a.d_o;
     auto off = [&](int u) {
       const int r = min(itm.qb * 64 + srow + 16 * u, nrows - 1);
@@ -551,23 +545,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
     st.lse = (itm.s ? a.lse_x : a.lse)[si];
     st.delta = (itm.s ? a.delta_x : a.delta)[si];
   };
-  auto qrow = [&](uint4 raw, const float *al, const float *be) {
-    const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t o4[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const int d = sd0 + 2 * e2;
-      o4[e2] = pack2(al[d] * bf16_lo(qw[e2]) + be[d],
-                     al[d + 1] * bf16_hi(qw[e2]) + be[d + 1]);
-    }
-    return make_uint4(o4[0], o4[1], o4[2], o4[3]);
-  };
-  auto store = [&](const Stage &st, Cur cu) {
-    const Item itm = decode(cu);
-    const float *al = sm.ab[itm.hi][2 * itm.s];
-    const float *be = sm.ab[itm.hi][2 * itm.s + 1];
-    *(uint4 *)&sm.q[srow][sd0] = qrow(st.q0, al, be);
-    *(uint4 *)&sm.q[srow + 32][sd0] = qrow(st.q1, al, be);
+  auto store = [&](const Stage &st) {
+    // element-wise copies: a whole-struct copy made the compiler keep the
+    // staging sets in scratch memory
+    *(uint4 *)&sm.q[srow][sd0] = make_uint4(st.q0.x, st.q0.y, st.q0.z, st.q0.w);
+    *(uint4 *)&sm.q[srow + 32][sd0] = make_uint4(st.q1.x, st.q1.y, st.q1.z, st.q1.w);
     *(uint4 *)&sm.g[srow][sd0] = st.g0;
     *(uint4 *)&sm.g[srow + 32][sd0] = st.g1;
     if (tid < 64) {
@@ -681,15 +663,15 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
   load(sB, c2);
   c2 = adv(c2);
   for (; c0.it + 1 < n_it;) {
-    __syncthreads();  // readers of the previous block are done (and ab)
-    store(sA, c0);
+    __syncthreads();  // readers of the previous block are done
+    store(sA);
     __syncthreads();
     load(sA, c2);
     c2 = adv(c2);
     block(c0);
     c0 = adv(c0);
     __syncthreads();
-    store(sB, c0);
+    store(sB);
     __syncthreads();
     load(sB, c2);
     c2 = adv(c2);
@@ -698,7 +680,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
   }
   if ((n_it & 1) == 1) {
     __syncthreads();
-    store(sA, c0);
+    store(sA);
     __syncthreads();
     block(c0);
   }

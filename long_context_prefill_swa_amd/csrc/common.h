@@ -121,6 +121,9 @@ struct BwdStreamArgs {
   const uint16_t *k_cache, *v_cache;    // [B, n_kv, cap, D]
   const float *alpha, *beta;            // [Hq*D]
   uint16_t *dq;                         // [B, nrows, Hq, D] d q_pre
+  uint16_t *qa;                         // [B, nrows, Hq, D] written: the
+                                        // query operand bf16((alpha q_pre +
+                                        // beta) log2(e) / sqrt(D))
   float *lse, *delta;                   // [B, Hq, nrows] base-2 lse, dO . o
   float *part;                          // [B, ceil(nrows/32), Hq, 2, D]
   int nrows, Hq, n_kv, n_keys, W, q_offset;  // W <= n_keys
@@ -128,8 +131,8 @@ struct BwdStreamArgs {
 };
 // Both streams, for dK and dV [B, T, n_kv, D].
 struct BwdKvArgs {
-  const uint16_t *q, *qx, *d_o, *d_ox, *k_cache, *v_cache;
-  const float *alpha, *beta, *alpha_x, *beta_x;
+  const uint16_t *qa, *qax;  // query operands the dQ kernels wrote
+  const uint16_t *d_o, *d_ox, *k_cache, *v_cache;
   const float *lse, *delta, *lse_x, *delta_x;
   uint16_t *dk, *dv;
   int T, T_out, Hq, n_kv, W;  // W <= T

@@ -726,7 +726,7 @@ int orthros_check_device_errors(void *stream) {
 namespace {
 
 struct BwdWs {
-  size_t lse, delta, lse_x, delta_x, part, part_x, total;
+  size_t lse, delta, lse_x, delta_x, part, part_x, qa, qa_x, total;
 };
 
 size_t al256(size_t n) { return (n + 255) & ~size_t(255); }
@@ -747,6 +747,10 @@ BwdWs bwd_ws(int B, int T, int T_out, int Hq, int D) {
   off += al256((size_t)B * ((T + 31) / 32) * Hq * 2 * D * 4);
   w.part_x = off;
   off += al256((size_t)B * ((T_out + 31) / 32) * Hq * 2 * D * 4);
+  w.qa = off;  // the query operands (bf16) the dQ kernels pass on
+  off += al256((size_t)B * T * Hq * D * 2);
+  w.qa_x = off;
+  off += al256((size_t)B * T_out * Hq * D * 2);
   w.total = off;
   return w;
 }
@@ -832,6 +836,7 @@ int orthros_attn_backward(
   sa.lse = (float *)(base + w.lse);
   sa.delta = (float *)(base + w.delta);
   sa.part = (float *)(base + w.part);
+  sa.qa = (uint16_t *)(base + w.qa);
   sa.nrows = T;
   sa.Hq = Hq;
   sa.n_kv = Hkv;
@@ -852,6 +857,7 @@ int orthros_attn_backward(
     sx.lse = (float *)(base + w.lse_x);
     sx.delta = (float *)(base + w.delta_x);
     sx.part = (float *)(base + w.part_x);
+    sx.qa = (uint16_t *)(base + w.qa_x);
     sx.nrows = T_out;
     sx.W = T;
     sx.q_offset = T - T_out;
@@ -859,16 +865,12 @@ int orthros_attn_backward(
     if (e != hipSuccess) return hip_fail("backward dq launch (output stream)", e);
   }
   BwdKvArgs ka;
-  ka.q = (const uint16_t *)q_pre;
-  ka.qx = (const uint16_t *)qx_pre;
+  ka.qa = (const uint16_t *)(base + w.qa);
+  ka.qax = (const uint16_t *)(base + w.qa_x);
   ka.d_o = (const uint16_t *)d_o;
   ka.d_ox = (const uint16_t *)d_ox;
   ka.k_cache = (const uint16_t *)k_cache;
   ka.v_cache = (const uint16_t *)v_cache;
-  ka.alpha = alpha;
-  ka.beta = beta;
-  ka.alpha_x = alpha_x;
-  ka.beta_x = beta_x;
   ka.lse = sa.lse;
   ka.delta = sa.delta;
   ka.lse_x = (float *)(base + w.lse_x);
