@@ -15,9 +15,10 @@
 // 32-wide contraction split 8 per g4; C holds rows 4 g4 .. 4 g4 + 3 of
 // column col):
 //  * bwd_dq_kernel (per stream): 8 waves, each 32 query rows of one head.
-//    Pass 1 over the band's 64-key tiles forms S^T = K Q^T and the row's
-//    log-sum-exp; pass 2 forms S^T and dP^T = V dO^T again, dS^T, and
-//    dQ^T += K^T dS^T (K^T read with ds_read_b64_tr_b16). It writes
+//    One pass over the band's 64-key tiles forms S^T = K Q^T and
+//    dP^T = V dO^T, dS^T against a running row maximum, and
+//    dQ^T += K^T dS^T (K^T read with ds_read_b64_tr_b16), rescaled as the
+//    maximum grows and divided by the row sum at the end. It writes
 //    dq_pre, the row's log-sum-exp and dO . o, per 32-row block the
 //    channel sums that make d alpha and d beta, and the query operand it
 //    formed (bf16 of the scaled alpha q + beta) for the dK/dV kernel.
@@ -271,17 +272,22 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
     return wave_on && k_last >= lo_w && k_first <= p_w_last;
   };
 
-  // ---- pass 1: row maxima and sums ----------------------------------------
+  // ---- one pass: S^T, dP^T, dS^T and dQ^T with a running row maximum ------
+  // dQ = sum_j p_j (dp_j - delta) k_j with p_j = 2^(s_j - lse). With the row
+  // maximum m and sum l of the keys seen so far, the pass accumulates
+  // acc = sum_j 2^(s_j - m) (dp_j - delta) k_j, rescaling acc and l when m
+  // grows (as the forward's online softmax does), and divides by l at the
+  // end; lse = m + log2(l) comes out of the same pass.
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     next_tile(kt);
-    load(kt < kt_hi ? kt + 1 : kt_lo);  // pass 2 starts over at kt_lo
+    if (kt < kt_hi) load(kt + 1);
     if (!wave_needs(kt)) continue;
     const bool inside = tile_inside(kt);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      f32x4 s[4];
+      f32x4 sv[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[kb] = scores_raw(kb, h2);
+      for (int kb = 0; kb < 4; ++kb) sv[kb] = scores_raw(kb, h2);
       __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
@@ -290,73 +296,43 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
       }
       if (!inside)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) mask(s[kb], kt, kb, h2);
+        for (int kb = 0; kb < 4; ++kb) mask(sv[kb], kt, kb, h2);
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, s[kb][i]);
+        for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sv[kb][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mn = fmaxf(m[h2], tmax);
       const float ms = (mn == -INFINITY) ? 0.0f : mn;
+      // 0 while the row has seen no key (acc and l are still zero)
+      const float corr = __builtin_amdgcn_exp2f(m[h2] - ms);
+      m[h2] = mn;
       float ps = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ps += __builtin_amdgcn_exp2f(s[kb][i] - ms);
-      l[h2] = l[h2] * __builtin_amdgcn_exp2f(m[h2] - ms) + ps;
-      m[h2] = mn;
-    }
-  }
-  // row log-sum-exp (base 2) over the four lane groups
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    float lt = l[h2];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
-    lse[h2] = m[h2] + __log2f(lt);
-  }
-
-  // ---- pass 2: dS^T and dQ^T ------------------------------------------------
-  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    next_tile(kt);
-    if (kt < kt_hi) load(kt + 1);
-    if (!wave_needs(kt)) continue;
-    const bool inside = tile_inside(kt);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
+      for (int dt = 0; dt < 8; ++dt) acc[h2][dt] *= corr;
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        f32x4 sv[2], dp[2];
+        f32x4 dp[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int kb = 2 * kp + half;
-          sv[half] = scores_raw(kb, h2);
           dp[half] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4)
             dp[half] = mfma16(lds_row8(sm.v, 16 * kb + col, c4, g4), doop[h2][c4], dp[half]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int g = 0; g < 16; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
         bf16x8 dsop;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          if (!inside) mask(sv[half], kt, 2 * kp + half, h2);
+        for (int half = 0; half < 2; ++half)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            // masked keys (and rows with no key at all) give p = 0
-            const float p = sv[half][i] == -INFINITY
-                                ? 0.0f
-                                : __builtin_amdgcn_exp2f(sv[half][i] - lse[h2]);
-            dsop[4 * half + i] = (__bf16)(p * (dp[half][i] - delta[h2]));
+            // masked keys give 2^(-inf) = 0
+            const float pt = __builtin_amdgcn_exp2f(sv[2 * kp + half][i] - ms);
+            ps += pt;
+            dsop[4 * half + i] = (__bf16)(pt * (dp[half][i] - delta[h2]));
           }
-        }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
           acc[h2][dt] = mfma16(lds_tr8(sm.k, 32 * kp, g4, j16, dt), dsop, acc[h2][dt]);
@@ -368,7 +344,18 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      l[h2] = l[h2] * corr + ps;
     }
+  }
+  // row sums over the four lane groups, log-sum-exp (base 2), 1 / l
+  float inv_l[2];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    float lt = l[h2];
+    lt += __shfl_xor(lt, 16, 64);
+    lt += __shfl_xor(lt, 32, 64);
+    lse[h2] = m[h2] + __log2f(lt);
+    inv_l[h2] = lt > 0.0f ? 1.0f / lt : 0.0f;
   }
 
   // ---- outputs ---------------------------------------------------------------
@@ -396,7 +383,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
       float g[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float dq = row_ok[h2] ? acc[h2][dt][i] * inv_sqrt_d : 0.0f;
+        const float dq = row_ok[h2] ? acc[h2][dt][i] * (inv_l[h2] * inv_sqrt_d) : 0.0f;
         g[i] = alv[i] * dq;
         sa[dt][i] += dq * qv[i];
         sb[dt][i] += dq;
@@ -582,6 +569,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkv_kernel(
         del4[h2] = *(const float4 *)&sm.delta[rq0 + 4 * g4];
         sc[h2] = dp[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+      if (none[0] & none[1]) continue;  // no key of the wave in this half
       auto quarter = [&](int h2) {
         const int rq0 = 32 * half + 16 * h2;
 #pragma unroll
