@@ -119,6 +119,68 @@ def shader_clock(dev, iters=100000):
     return cycles / (ticks / (khz.value * 1e3)) / 1e6
 
 
+def hbm_reference(dev, flush, reps=10):
+    """The HBM rate plain streaming kernels reach on this GPU
+    (libclock_probe.so: buffer loads and stores, each launch after a MALL
+    flush), as a second reference beside the published 8 TB/s: a read of
+    512 MiB (the 128K cache's K and V) and a copy moving 2.68 GB (the bytes
+    of the W = 128 window pass). None if the probe is not built."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "long_context_prefill_swa_amd",
+                        "libclock_probe.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.hbm_read_probe.argtypes = [vp, sz, i32, vp, vp]
+    L.hbm_copy_probe.argtypes = [vp, vp, sz, i32, vp]
+    L.hbm_read_probe.restype = L.hbm_copy_probe.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev)
+    st = ctypes.c_void_p(stream.cuda_stream)
+    read_bytes, read_wg = 512 << 20, 256
+    copy_bytes, copy_wg = 1342177280, 4096
+    src = torch.ones(copy_bytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(read_wg * 256 * 4, dtype=torch.int32, device=dev)
+
+    def timed(f):
+        for _ in range(2):
+            if f() != 0:
+                raise RuntimeError("hbm probe launch failed")
+        ts = []
+        for _ in range(reps):
+            flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return stats([x.elapsed_time(y) for x, y in ts])
+
+    s_read = timed(lambda: L.hbm_read_probe(ctypes.c_void_p(src.data_ptr()),
+                                            read_bytes, read_wg,
+                                            ctypes.c_void_p(sink.data_ptr()), st))
+    s_copy = timed(lambda: L.hbm_copy_probe(ctypes.c_void_p(src.data_ptr()),
+                                            ctypes.c_void_p(dst.data_ptr()),
+                                            copy_bytes, copy_wg, st))
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    read_gbps = read_bytes / (s_read["median"] * 1e-3) / 1e9
+    copy_gbps = 2 * copy_bytes / (s_copy["median"] * 1e-3) / 1e9
+    return {"read_GBps": read_gbps, "read_bytes": read_bytes,
+            "read_ms": s_read, "copy_GBps": copy_gbps,
+            "copy_bytes_moved": 2 * copy_bytes, "copy_ms": s_copy,
+            "read_frac_of_peak": read_gbps / PEAK_HBM_GBPS,
+            "copy_frac_of_peak": copy_gbps / PEAK_HBM_GBPS,
+            "notes": "hand-written streaming read and copy kernels "
+                     "(libclock_probe.so), medians, each launch after a MALL "
+                     "flush"}
+
+
 def run_context(dev, clock_before, clock_after):
     import torch
     cpu = ""
@@ -302,6 +364,11 @@ def main():
                       "decode_pair_b64": "B=64 Hq=32 Hkv=8 D=128 L0=32768 W=2048 steps=256",
                       "global_batch": pc.B, "seq_len": pc.T}}
     out["run"] = run_context(dev, clock_before, clock_after)
+    ref = hbm_reference(dev, mall_flush)
+    if ref is not None:
+        out["hbm_reference"] = ref
+        log(f"[bench] HBM reference: read {ref['read_GBps']:.0f} GB/s, "
+            f"copy {ref['copy_GBps']:.0f} GB/s")
     log(f"[bench] wall {wall:.2f}s, events {total_ms:.1f} ms")
 
     if run_prefill:
@@ -349,6 +416,10 @@ def main():
             "traffic": traffic_from_profile("splitkv_global_128k", sha_g),
             "algorithmic_bytes_per_launch": kv_bytes,
             "avg_launch_ms": t_glob, "kernel_source_sha256": sha_g}
+        if "hbm_reference" in out:  # against the measured streaming read
+            out["roofline_global"]["frac_of_measured_read"] = (
+                out["roofline_global"]["achieved"]
+                / out["hbm_reference"]["read_GBps"])
         log(f"[bench] prefill: append {t_app:.3f} ms, swa {t_swa:.3f} ms "
             f"({swa_tflops:.1f} TFLOP/s), global {t_glob:.3f} ms from HBM, "
             f"{s_glob_warm['mean']:.3f} ms warm")
@@ -383,6 +454,9 @@ def main():
             "traffic": traffic_from_profile("splitkv_decode_b64", sha_s),
             "algorithmic_bytes_per_launch": step_bytes,
             "avg_launch_ms": t_dec / n_dec, "kernel_source_sha256": sha_s}
+        if "hbm_reference" in out:
+            out["roofline_decode"]["frac_of_measured_read"] = (
+                gbps / out["hbm_reference"]["read_GBps"])
         log(f"[bench] decode: {t_dec / n_dec:.3f} ms/step, {gbps:.0f} GB/s")
         if not run_prefill:
             out["value"] = None
@@ -441,6 +515,9 @@ def main():
                 "traffic": traffic_from_profile("band_roll_prefill_128k_w128",
                                                 kernel_sha(ROLL_SRC)),
                 "kernel_source_sha256": kernel_sha(ROLL_SRC)}}
+        if "hbm_reference" in out:  # against the measured copy (reads+writes)
+            out["swa_w128"]["roofline"]["frac_of_measured_copy"] = (
+                out["swa_w128"]["gbps"] / out["hbm_reference"]["copy_GBps"])
         log(f"[bench] swa W=128: {t_s:.3f} ms, "
             f"{out['swa_w128']['gbps']:.0f} GB/s")
 
