@@ -16,9 +16,10 @@
 // column col):
 //  * bwd_dq_kernel (per stream): 8 waves, each 32 query rows of one head.
 //    One pass over the band's 64-key tiles forms S^T = K Q^T and
-//    dP^T = V dO^T, dS^T against a running row maximum, and
-//    dQ^T += K^T dS^T (K^T read with ds_read_b64_tr_b16), rescaled as the
-//    maximum grows and divided by the row sum at the end. It writes
+//    dP^T = V dO^T, dS^T against a reference row maximum, and
+//    dQ^T += K^T dS^T (K^T read with ds_read_b64_tr_b16), rescaled when a
+//    tile's maximum passes the reference by more than 2^8 (then the
+//    reference moves) and divided by the row sum at the end. It writes
 //    dq_pre, the row's log-sum-exp and dO . o, per 32-row block the
 //    channel sums that make d alpha and d beta, and the query operand it
 //    formed (bf16 of the scaled alpha q + beta) for the dK/dV kernel.
@@ -229,9 +230,11 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
     }
   }
 
-  // S^T block (16 keys of sub-block kb x 16 rows of half h2), masked
+  // S^T block (16 keys of sub-block kb x 16 rows of half h2) minus the
+  // row's reference maximum (the accumulator starts at -m)
+  float negm[2] = {0.0f, 0.0f};
   auto scores_raw = [&](int kb, int h2) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    f32x4 s = {negm[h2], negm[h2], negm[h2], negm[h2]};
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4)
       s = mfma16(lds_row8(sm.k, 16 * kb + col, c4, g4), qop[h2][c4], s);
@@ -252,7 +255,12 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
            r0 + 32 <= a.nrows;
   };
 
+  // m: the reference maximum, moved only when a tile's maximum exceeds it
+  // by more than kTau (then acc and l are rescaled); thr: -inf while the
+  // row has seen no key, then kTau
+  constexpr float kTau = 8.0f;
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.0f, 0.0f};
+  float thr[2] = {-INFINITY, -INFINITY};
   float lse[2] = {0.0f, 0.0f};
   f32x4 acc[2][8];
 #pragma unroll
@@ -272,12 +280,15 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
     return wave_on && k_last >= lo_w && k_first <= p_w_last;
   };
 
-  // ---- one pass: S^T, dP^T, dS^T and dQ^T with a running row maximum ------
-  // dQ = sum_j p_j (dp_j - delta) k_j with p_j = 2^(s_j - lse). With the row
-  // maximum m and sum l of the keys seen so far, the pass accumulates
-  // acc = sum_j 2^(s_j - m) (dp_j - delta) k_j, rescaling acc and l when m
-  // grows (as the forward's online softmax does), and divides by l at the
-  // end; lse = m + log2(l) comes out of the same pass.
+  // ---- one pass: S^T, dP^T, dS^T and dQ^T against a reference maximum ------
+  // dQ = sum_j p_j (dp_j - delta) k_j with p_j = 2^(s_j - lse). With a
+  // reference maximum m and the sum l of the keys seen so far, the pass
+  // accumulates acc = sum_j 2^(s_j - m) (dp_j - delta) k_j and divides by l
+  // at the end; lse = m + log2(l) comes out of the same pass. As in the
+  // forward kernels m moves (and acc and l are rescaled) only when a tile's
+  // maximum exceeds it by more than kTau, so the exponents stay <= kTau;
+  // the score and dP accumulators start at -m and -delta, so neither
+  // needs a subtraction per element.
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     next_tile(kt);
     if (kt < kt_hi) load(kt + 1);
@@ -304,21 +315,31 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
         for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sv[kb][i]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m[h2], tmax);
-      const float ms = (mn == -INFINITY) ? 0.0f : mn;
-      // 0 while the row has seen no key (acc and l are still zero)
-      const float corr = __builtin_amdgcn_exp2f(m[h2] - ms);
-      m[h2] = mn;
-      float ps = 0.0f;
+      const bool need = tmax > thr[h2];
+      if (__any(need)) {
+        const float shift = need ? tmax : 0.0f;
+        // 0 while the row has seen no key (acc and l are still zero)
+        const float corr =
+            need ? ((m[h2] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(-shift))
+                 : 1.0f;
+        m[h2] = need ? ((m[h2] == -INFINITY) ? shift : m[h2] + shift) : m[h2];
+        l[h2] *= corr;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[h2][dt] *= corr;
+        for (int dt = 0; dt < 8; ++dt) acc[h2][dt] *= corr;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sv[kb] -= shift;
+        negm[h2] = (m[h2] == -INFINITY) ? 0.0f : -m[h2];
+        thr[h2] = (m[h2] == -INFINITY) ? -INFINITY : kTau;
+      }
+      float ps = 0.0f;
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
         f32x4 dp[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int kb = 2 * kp + half;
-          dp[half] = f32x4{0.f, 0.f, 0.f, 0.f};
+          // dP - delta: the accumulator starts at -delta (the row's dO . o)
+          dp[half] = f32x4{-delta[h2], -delta[h2], -delta[h2], -delta[h2]};
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4)
             dp[half] = mfma16(lds_row8(sm.v, 16 * kb + col, c4, g4), doop[h2][c4], dp[half]);
@@ -329,9 +350,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             // masked keys give 2^(-inf) = 0
-            const float pt = __builtin_amdgcn_exp2f(sv[2 * kp + half][i] - ms);
+            const float pt = __builtin_amdgcn_exp2f(sv[2 * kp + half][i]);
             ps += pt;
-            dsop[4 * half + i] = (__bf16)(pt * (dp[half][i] - delta[h2]));
+            dsop[4 * half + i] = (__bf16)(pt * dp[half][i]);
           }
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
@@ -344,7 +365,7 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      l[h2] = l[h2] * corr + ps;
+      l[h2] += ps;
     }
   }
   // row sums over the four lane groups, log-sum-exp (base 2), 1 / l
