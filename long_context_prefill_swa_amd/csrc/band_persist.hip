@@ -325,10 +325,25 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
                                                            0, 0, 0);
         }
     };
-    // Band mask (only tiles crossing a band edge of some row of this wave),
-    // row maximum, and the lazy move of the reference maximum. The tile
-    // offset is a 32-bit uniform value, so the band test is scalar.
-    auto settle = [&](f32x16 (&sn)[2], int kb) __attribute__((always_inline)) {
+    // Row maximum of this lane's 32 scores (four independent chains), and
+    // the maximum across the lane pair.
+    auto tile_max = [&](const f32x16 (&sn)[2]) __attribute__((always_inline)) {
+      float t4[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        t4[c] = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          t4[c] = fmaxf(t4[c], sn[c >> 1][8 * (c & 1) + v]);
+      }
+      return max_xor32(fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3])));
+    };
+    // Band mask (only tiles crossing a band edge of some row of this wave)
+    // and the lazy move of the reference maximum. tmax is the tile's
+    // maximum over all its keys, taken before the mask; a masked tile takes
+    // it again. The tile offset is a 32-bit uniform value, so the band test
+    // is scalar.
+    auto settle = [&](f32x16 (&sn)[2], int kb, float tmax) __attribute__((always_inline)) {
       const bool inside = kb >= wpos_hi - W + 1 && kb + kBN - 1 <= wpos_lo;
       if (!inside) {
         const int d0 = (int)(kb - tq);
@@ -339,18 +354,8 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
             const int d = d0 + 32 * sk + 8 * (v >> 2) + 4 * hh + (v & 3);
             sn[sk][v] = (d > 0 || d <= -W) ? -INFINITY : sn[sk][v];
           }
+        tmax = tile_max(sn);  // the maximum over the keys in range
       }
-      // four independent chains over this lane's 32 scores
-      float t4[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        t4[c] = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-          t4[c] = fmaxf(t4[c], sn[c >> 1][8 * (c & 1) + v]);
-      }
-      float tmax = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
-      tmax = max_xor32(tmax);
       const bool need = tmax > thr;
       if (__any(need)) {
         const float shift = need ? tmax : 0.0f;
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     if (n < n_last && !q_in_loop) load_qblock(seg + (n + 1) * n_segs);
     f32x16 sa[2], sb[2];
     scores(sa, 0);
-    settle(sa, kt0 * kBN);
+    settle(sa, kt0 * kBN, tile_max(sa));
     __syncthreads();  // K buffer 0 is refilled at the end of step 0
 
     // Software pipeline, one 64-key tile per step (the banded kernel's).
@@ -415,6 +420,9 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
         }
       }
       const int vb = it & 1;
+      // the next tile's maximum over all its keys, between the P V MFMAs
+      // (edge tiles mask and take it again in the settle)
+      const float tmax_next = tile_max(sn);
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
@@ -440,8 +448,9 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
       for (int g = 0; g < 16; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // V^T reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // P V MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // the maximum
       }
-      settle(sn, kb + kBN);
+      settle(sn, kb + kBN, tmax_next);
       store_k(r_in, it & 1);     // K of tile it+2
       store_v(r_in, vb ^ 1);     // V of tile it+1
       // All but this step's four tile loads are complete (the counter
