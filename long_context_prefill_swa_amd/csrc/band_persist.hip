@@ -128,11 +128,13 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   const int hs = w % kGs, ps = w / kGs;
   const int64_t head_off = ((int64_t)b * n_kv + kvh) * cap * D;
 
-  // alpha / beta of the group's heads
+  // alpha / beta of the group's heads, times log2(e) / sqrt(D) (the
+  // softmax runs in base 2)
+  const float qs = kLog2e * rsqrtf((float)D);
   for (int i = tid; i < kGs * 2 * D; i += kNT) {
     const int s = i / (2 * D), which = (i / D) & 1, d = i % D;
     const int h = max((int)groups.q[gi][s], 0);
-    sm.ab[s][which][d] = (which ? beta : alpha)[h * D + d];
+    sm.ab[s][which][d] = (which ? beta : alpha)[h * D + d] * qs;
   }
 
   // ---- query block in, output block out (LDS <-> HBM, whole rows) ---------
@@ -256,7 +258,6 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   const int v_row0 = 4 * hh + (j16 >> 2);          // + 16 kg (+ 8 second read)
   const int v_col0 = 16 * (g16 & 1) + 4 * (j16 & 3);  // + 32 dt
 
-  const float qs = kLog2e * rsqrtf((float)D);
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // ---- query operand from the block in LDS (B of S^T) ----------------------
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
         for (int e = 0; e < 8; ++e) {
           const float qv = bf16_bits_to_f32((e & 1) ? (wv[e >> 1] >> 16)
                                                     : (wv[e >> 1] & 0xffffu));
-          qop[c][e] = (__bf16)((al[d0 + e] * qv + be[d0 + e]) * qs);
+          qop[c][e] = (__bf16)(al[d0 + e] * qv + be[d0 + e]);
         }
       }
   };
@@ -343,7 +344,10 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     // maximum over all its keys, taken before the mask; a masked tile takes
     // it again. The tile offset is a 32-bit uniform value, so the band test
     // is scalar.
-    auto settle = [&](f32x16 (&sn)[2], int kb, float tmax) __attribute__((always_inline)) {
+    // (first: the item's first tile; the accumulators and row sums are
+    // still zero, so nothing is rescaled)
+    auto settle = [&](f32x16 (&sn)[2], int kb, float tmax, bool first = false)
+        __attribute__((always_inline)) {
       const bool inside = kb >= wpos_hi - W + 1 && kb + kBN - 1 <= wpos_lo;
       if (!inside) {
         const int d0 = (int)(kb - tq);
@@ -363,10 +367,12 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
             need ? ((m == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(-shift))
                  : 1.0f;
         m = need ? ((m == -INFINITY) ? shift : m + shift) : m;
+        if (!first) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) l4[c] *= corr;
+          for (int c = 0; c < 4; ++c) l4[c] *= corr;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
+          for (int dt = 0; dt < 4; ++dt) acc[dt] *= corr;
+        }
 #pragma unroll
         for (int sk = 0; sk < 2; ++sk) sn[sk] -= shift;
         const float nm = (m == -INFINITY) ? 0.0f : -m;
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     if (n < n_last && !q_in_loop) load_qblock(seg + (n + 1) * n_segs);
     f32x16 sa[2], sb[2];
     scores(sa, 0);
-    settle(sa, kt0 * kBN, tile_max(sa));
+    settle(sa, kt0 * kBN, tile_max(sa), true);
     __syncthreads();  // K buffer 0 is refilled at the end of step 0
 
     // Software pipeline, one 64-key tile per step (the banded kernel's).
