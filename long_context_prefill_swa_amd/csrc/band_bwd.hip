@@ -82,6 +82,22 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)b) << 16);
 }
 
+// Sum over the 16 lanes of a row (lanes 16 k .. 16 k + 15), left in every
+// one of them: four DPP adds (pairs, then quads, then the two halves by
+// mirroring), no LDS permutes.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return v;
+}
+
 // Block -> (unit, (batch, head group) pair). Workgroups are dealt to the
 // 8 XCDs by block id; when the pairs are a multiple of 8, pair p's units
 // (row tiles or key blocks) all run on XCD p % 8, so the rows they share
@@ -423,11 +439,8 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        sa[dt][i] += __shfl_xor(sa[dt][i], off, 64);
-        sb[dt][i] += __shfl_xor(sb[dt][i], off, 64);
-      }
+      sa[dt][i] = sum16(sa[dt][i]);
+      sb[dt][i] = sum16(sb[dt][i]);
     }
   if (col == 0) {
     const int n_rb = (a.nrows + 31) / 32;
