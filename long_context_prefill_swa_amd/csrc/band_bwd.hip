@@ -137,6 +137,9 @@ __global__ __launch_bounds__(512, 2) void bwd_dq_kernel(BwdStreamArgs a,
   const int n_wg_rows = (a.nrows + kRowsWg - 1) / kRowsWg;
   int wr, rest;
   xcd_unit(n_wg_rows, wr, rest);
+  // a row tile's band never shrinks with its index (the window's start,
+  // or the prefix of an unbounded window): the longest tiles start first
+  wr = n_wg_rows - 1 - wr;
   const int gi = rest % groups.n_groups;
   const int b = rest / groups.n_groups;
 
