@@ -10,10 +10,10 @@
 // launch of the next workgroup on the compute unit, the query load from
 // HBM, the first tiles' round trip, and the output written as 8-byte pieces
 // of 32 rows per instruction. Here a workgroup stays resident and walks 64-row
-// query tiles ("items") of one (batch, KV head), one per round of S
-// consecutive tiles for S workgroups per (batch, KV head), all on one XCD,
-// so that the S workgroups of a KV head work on neighbouring tiles whose
-// bands share the XCD's L2. Per item:
+// query tiles ("items") of one (batch, KV head): tiles seg, seg + S, ...
+// for S workgroups per (batch, KV head), all on one XCD, so that the S
+// workgroups of a KV head work on neighbouring tiles whose bands share the
+// XCD's L2. Per item:
 //  * the query block (64 rows x 4 heads) was brought into LDS by direct
 //    global-to-LDS loads (global_load_lds_dwordx4) issued early in the
 //    previous item's tile loop;
