@@ -118,18 +118,8 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   if (pair >= per || seg >= n_qtiles) return;
   const int gi = pair % groups.n_groups;
   const int b = pair / groups.n_groups;
-  // Item n of this workgroup is a query tile of round n (tiles n n_segs ..
-  // n n_segs + n_segs - 1): tile seg in even rounds and, in odd rounds that
-  // are complete, tile n_segs - 1 - seg of the round. The first tiles of a
-  // sequence see fewer keys than the window, so dealing alternate rounds in
-  // reverse pairs short tiles with long ones and evens out the work of the
-  // workgroups of a KV head.
+  // items seg, seg + n_segs, ...: item number n is query tile seg + n n_segs
   const int n_last = (n_qtiles - 1 - seg) / n_segs;
-  auto qt_of = [&](int n) __attribute__((always_inline)) {
-    return ((n & 1) && (n + 1) * n_segs <= n_qtiles)
-               ? (n + 1) * n_segs - 1 - seg
-               : seg + n * n_segs;
-  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,7 +195,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
   };
   auto item_of = [&](int n) __attribute__((always_inline)) {
     Item it;
-    it.qt = qt_of(n);
+    it.qt = seg + n * n_segs;
     // rows r0 .. r0 + 63 sit at positions pos_off + r0 ...
     const int r0 = it.qt * kItemRows;
     const int p0 = pos_off + r0;
@@ -404,7 +394,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     // step's MFMAs, and it is older than that step's tile loads, whose wait
     // gives it a whole step), else here.
     const bool q_in_loop = ntiles >= 4;
-    if (n < n_last && !q_in_loop) load_qblock(qt_of(n + 1));
+    if (n < n_last && !q_in_loop) load_qblock(seg + (n + 1) * n_segs);
     f32x16 sa[2], sb[2];
     scores(sa, 0);
     settle(sa, kt0 * kBN, tile_max(sa), true);
@@ -478,7 +468,7 @@ __global__ __launch_bounds__(kNT, 2) void band_persist_kernel(
     int it = 0;
     for (; it + 1 < ntiles; it += 2) {
       if (it == 2 && q_in_loop && n < n_last)
-        load_qblock(qt_of(n + 1));
+        load_qblock(seg + (n + 1) * n_segs);
       step(sa, sb, ra, rb, it);
       step(sb, sa, rb, ra, it + 1);
     }
